@@ -1,0 +1,245 @@
+"""Benchmark of the paged-KV hot path on one MI355X.
+
+A step is one pass of the whole path over one batch, as an engine runs it:
+host step preparation (slot mapping, lengths, padded block tables) into
+pinned buffers, upload, kv_store of the step's K/V, then attention.
+
+Headline (``value``): the decode step of the 256-sequence decode workload
+(contexts U[100, 2048], 16 Q / 8 KV heads, head dim 128, bf16, block 256,
+batch padded to 272 rows) in GB/s of algorithmic HBM bytes (K/V context read
+once, q, out, block-table entries and lengths, plus 8 KiB stored per real
+token) per wall-clock step. ``roofline`` reports the decode attention call
+(split-K kernel + merge kernel) timed with HIP events on its stream against
+the 8 TB/s HBM peak. ``prefill`` reports the chunked-prefill step (16384-token
+budget) in TFLOP/s of unmasked attention flops against the 2.5 PFLOP/s bf16
+MFMA peak. ``cpu_baseline`` times the fp64 oracle on the same decode step
+on the host before the GPU is initialised.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (what the method must move / compute; no implementation overhead)
+# ----------------------------------------------------------------------------
+
+def decode_bytes(w: W.Workload) -> dict:
+    p = w.passes[0].batch
+    real = p.seqs
+    rows = len(real) + p.num_pad
+    kv = sum(s.seq_len for s in real) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * rows * w.num_q_heads * w.head_dim * 2
+    bt = sum(-(-s.seq_len // w.block_size) for s in real) * 4 + rows * 4
+    store = sum(s.seq_len - s.num_cached for s in real) * w.num_kv_heads * w.head_dim * 2 * 4
+    return {"attn": kv + qo + bt, "store": store, "kv": kv}
+
+
+def prefill_work(w: W.Workload) -> dict:
+    p = w.passes[0].batch
+    pairs = 0
+    for s in p.seqs:
+        n, c = s.seq_len - s.num_cached, s.num_cached
+        pairs += n * c + n * (n + 1) // 2
+    flops = 4 * w.head_dim * w.num_q_heads * pairs
+    tokens = sum(s.seq_len - s.num_cached for s in p.seqs)
+    store = tokens * w.num_kv_heads * w.head_dim * 2 * 4
+    return {"flops": flops, "pairs": pairs, "store": store, "tokens": tokens}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, on the host, before any GPU work
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(w: W.Workload) -> dict:
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from tests import oracle_side as O
+    from oracle import paged as op
+
+    log("[bench] cpu baseline: building the oracle's caches on the host ...")
+    t = time.perf_counter()
+    # setup (history) stores are not part of a step
+    w_setup_only = W.Workload(w.name, w.seed, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                              w.num_blocks, w.max_blocks_per_seq, w.setup, W.Batch([], stream=999), [])
+    kc, vc = O.build_caches(w_setup_only, device="cpu")
+    k, v = W.store_kv(w, "cpu")
+    kb, vb = O.bits(k), O.bits(v)
+    p = w.passes[0]
+    q = O.bits(W.pass_q(w, p, "cpu"))
+    log(f"[bench] cpu baseline: inputs ready in {time.perf_counter() - t:.1f}s; timing the oracle step")
+
+    def run():
+        slots, cu, ctx, bt = O.metadata(w, p.batch)
+        kc2, vc2 = op.kv_store_ref(kc, vc, kb, vb, slots)
+        return op.decode_ref(q, kc2, vc2, bt, ctx, w.scale)
+
+    cores = 1
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            run()
+            dt = time.perf_counter() - t0
+    else:
+        t0 = time.perf_counter()
+        run()
+        dt = time.perf_counter() - t0
+        cores = os.cpu_count() or 1
+    b = decode_bytes(w)
+    gbs = (b["attn"] + b["store"]) / dt / 1e9
+    log(f"[bench] cpu baseline: oracle step {dt:.2f}s -> {gbs:.4f} GB/s")
+    return {"value": round(gbs, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": "one full decode step of the decode workload (store of 272 rows + decode of 256 "
+                      "sequences and 16 padding rows), fp64 numpy oracle, BLAS limited to 1 thread; "
+                      "host-generated values of the same shapes"}
+
+
+# ----------------------------------------------------------------------------
+# GPU timing
+# ----------------------------------------------------------------------------
+
+def time_steps(runner, steps: int, warmup: int, torch):
+    """Wall-clock K steps bracketed by synchronize; HIP events around the
+    store and the attention call of every step (on the launch stream)."""
+    from paged_kv_attention_28_amd import binding as B  # noqa: F401
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        runner.prepare_and_upload()
+        e = evs[i]
+        e[0].record()
+        runner.store_only()
+        e[1].record()
+        runner.attention_only()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    store_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    return wall / steps * 1e3, store_ms, attn_ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    wd = W.make(2)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wd)
+
+    import torch
+    from paged_kv_attention_28_amd import harness as H
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
+
+    # ---- decode step ----
+    log("[bench] decode workload: setup stores ...")
+    dw = H.DeviceWorkload(wd, dev)
+    dw.run_setup()
+    torch.cuda.synchronize()
+    runner = H.StepRunner(dw, wd.passes[0])
+    ms, store_ms, attn_ms = time_steps(runner, args.steps, args.warmup, torch)
+    db = decode_bytes(wd)
+    step_bytes = db["attn"] + db["store"]
+    value = step_bytes / (ms * 1e-3) / 1e9
+    attn_avg = float(attn_ms.mean())
+    achieved = db["attn"] / (attn_avg * 1e-3) / 1e9
+    log(f"[bench] decode step {ms * 1e3:.1f} us wall; store {store_ms.mean() * 1e3:.1f} us, "
+        f"attention {attn_avg * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
+
+    # ---- prefill step ----
+    prefill = None
+    if not args.no_prefill:
+        wp = W.make(3)
+        pw = prefill_work(wp)
+        dwp = H.DeviceWorkload(wp, dev)
+        dwp.run_setup()
+        torch.cuda.synchronize()
+        rp = H.StepRunner(dwp, wp.passes[0])
+        pms, pstore, pattn = time_steps(rp, max(args.steps // 2, 5), args.warmup, torch)
+        pav = float(pattn.mean())
+        tflops = pw["flops"] / (pav * 1e-3) / 1e12
+        store_gbs = pw["store"] / (float(pstore.mean()) * 1e-3) / 1e9
+        log(f"[bench] prefill step {pms * 1e3:.1f} us wall; store {pstore.mean() * 1e3:.1f} us "
+            f"({store_gbs:.0f} GB/s), attention {pav * 1e3:.1f} us -> {tflops:.1f} TFLOP/s "
+            f"({tflops / BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+        prefill = {"workload": "chunked prefill: 36 seqs, 16124 new tokens (budget 16384), prompts U[100,1024], "
+                               "about half with a shared 256/512-token cached prefix, first seq a mid-block chunk "
+                               "continuation; 16Q/8KV, d128, bf16, block 256",
+                   "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
+                   "attn_us": round(pav * 1e3, 2), "step_us_wall": round(pms * 1e3, 2),
+                   "store_us": round(float(pstore.mean()) * 1e3, 2), "store_gbs": round(store_gbs, 1),
+                   "flops": pw["flops"], "pairs": pw["pairs"]}
+
+    line = {
+        "metric": "decode attn GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v; no model weights)",
+        "config": {"workload": "decode: 256 seqs + 16 padding rows (272), context U[100,2048], GQA 16Q/8KV, "
+                               "head_dim 128, bf16, block 256, shuffled pool 1.25x; step = host prepare + upload "
+                               "+ kv_store + paged_attn_decode",
+                   "global_batch": 272, "seq_len": int(max(s.seq_len for s in wd.store.seqs)),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged_attn_decode (split-K + merge), HIP events, mean over timed steps",
+                     "algorithmic_bytes": db["attn"], "us": round(attn_avg * 1e3, 2)},
+        "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,205 @@
+/*
+ * pkv.h — C ABI of libpkv.so: paged KV-cache store and paged attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Page references:
+ *   P1 = "13. 读一个最小推理引擎：nano-vllm"
+ *   P2 = "读 Nano-vLLM 源码：一个极简 LLM 推理引擎是如何工作的"
+ *
+ * One attention layer owns two caches, K and V, each a preallocated bf16
+ * tensor [num_blocks, block_size = 256, num_kv_heads, head_dim = 128]
+ * (P1, "第五站：执行准备与 KV 容量": the cache is allocated once and never
+ * reallocated; block size 256, P1 "第二站：一个请求的状态"). Row `slot` of the
+ * flattened cache holds one token's K (or V) for all KV heads; byte offsets
+ * are computed in 64 bits.
+ *
+ * Conventions for every call:
+ *   - Pointers named "device" are caller-owned device memory (allocated by
+ *     any means, e.g. torch); "host" pointers are ordinary host memory. The
+ *     library never allocates or frees device memory and never synchronises.
+ *   - `stream` is a hipStream_t (NULL = the null stream); kernels are
+ *     enqueued on it and may still be running when the call returns.
+ *   - bf16 tensors are raw 16-bit bf16 bit patterns; integer metadata is int32.
+ *   - Errors are detected on the host before anything is launched. A call
+ *     returns PKV_OK or an error code and then pkv_last_error() (thread-local)
+ *     describes the failure. Nothing is launched on a non-OK return, except
+ *     PKV_ERR_HIP, which reports a failed launch.
+ *   - Device-side contents (slot values, block ids, lengths) are the caller's
+ *     contract and are not checked on the host; kernels never read or write
+ *     outside the cache for a slot or block id outside the pool (such rows
+ *     are skipped / read as masked), but results for such inputs are
+ *     unspecified.
+ *   - A call with zero work returns PKV_OK without launching.
+ *   - The only global state is the thread-local error message: calls from
+ *     different threads on different streams are independent.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID = 1,     /* bad argument: null pointer, negative count, bad lengths */
+  PKV_ERR_UNSUPPORTED = 2, /* valid but not supported: head_dim != 128, block_size != 256, alignment */
+  PKV_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_WORKSPACE = 4    /* workspace missing or smaller than the size query returned */
+};
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* ABI revision of this header; bumped on any signature change. */
+int32_t pkv_abi_version(void);
+#define PKV_ABI_VERSION 1
+
+/*
+ * pkv_prepare_step — per-step attention metadata, built on the host.
+ *
+ * P1, "第五站：执行准备与 KV 容量": the step preparation turns the scheduled
+ * sequences into the model's inputs, chiefly slot_mapping, one cache row per
+ * token computed this step: slot = block_table[pos / block_size] * block_size
+ * + pos % block_size. P1, "第二站：一个请求的状态": the tokens computed are those
+ * from num_cached onward (prefix hits, chunk continuations and decode alike).
+ * P1, "第五站" (CUDA Graph paragraph): padding rows of a replayed decode batch
+ * carry slot -1.
+ *
+ * Inputs (host):
+ *   num_seqs            real sequences, >= 0
+ *   seq_lens[s]         len(seq) including this step's tokens, >= 1
+ *   num_cached[s]       tokens already in the cache, 0 <= num_cached < seq_len
+ *   block_table_data    concatenated physical block ids of all sequences
+ *   block_table_offsets[s+1]  sequence s owns data[offsets[s] .. offsets[s+1]),
+ *                       at least ceil(seq_len / block_size) ids, each >= 0
+ *   num_pad             padding rows appended after the real sequences
+ *                       (one token each, slot -1, context length 0)
+ *   block_size          tokens per block (> 0)
+ *   max_blocks_per_seq  row stride of out_block_tables (>= every table length)
+ *   slot_capacity       entries available in out_slot_mapping
+ * Outputs (host, caller-allocated):
+ *   out_slot_mapping[T]                 T = sum(seq_len - num_cached) + num_pad
+ *   out_cu_seqlens_q[num_seqs+num_pad+1] prefix sums of tokens per row
+ *   out_context_lens[num_seqs+num_pad]   seq_len (0 for padding rows)
+ *   out_block_tables[(num_seqs+num_pad) * max_blocks_per_seq], -1 padded
+ *   out_num_tokens, out_max_q_len, out_max_context_len (may be NULL)
+ * Errors: PKV_ERR_INVALID for any violated condition above or a slot that
+ * does not fit in int32; outputs are then unspecified.
+ */
+pkv_status pkv_prepare_step(int32_t num_seqs, const int32_t* seq_lens, const int32_t* num_cached,
+                            const int32_t* block_table_data, const int64_t* block_table_offsets,
+                            int32_t num_pad, int32_t block_size, int32_t max_blocks_per_seq,
+                            int32_t* out_slot_mapping, int64_t slot_capacity,
+                            int32_t* out_cu_seqlens_q, int32_t* out_context_lens,
+                            int32_t* out_block_tables, int64_t* out_num_tokens,
+                            int32_t* out_max_q_len, int32_t* out_max_context_len);
+
+/*
+ * kv_store — scatter this step's K and V token rows into the paged caches.
+ *
+ * P1, "第六站：注意力层": before attention, for prefill and decode alike, each
+ * token's K and V rows (all KV heads) are copied to row slot_mapping[i] of
+ * the caches; a slot of -1 (a padding row) is skipped. The copy is bit-exact.
+ *
+ *   key, value       device bf16, token i's row starts at key + i * key_token_stride
+ *                    elements and holds num_kv_heads * head_dim contiguous
+ *                    elements (a strided view of a fused QKV buffer is fine)
+ *   key/value_token_stride  in elements; the byte stride must be a multiple of 16
+ *   k_cache, v_cache device bf16 [num_blocks, block_size, num_kv_heads, head_dim]
+ *   slot_mapping     device int32 [num_tokens]; -1 = skip. Any slot outside
+ *                    [0, num_blocks * block_size) is also skipped.
+ * Two tokens must not name the same slot in one call (the winner would be
+ * unspecified). All pointers 16-byte aligned.
+ * Errors: INVALID (null pointer, negative count), UNSUPPORTED (head_dim !=
+ * 128, block_size != 256, num_kv_heads outside 1..16, misalignment), HIP.
+ */
+pkv_status kv_store(const void* key, int64_t key_token_stride, const void* value,
+                    int64_t value_token_stride, void* k_cache, void* v_cache,
+                    const int32_t* slot_mapping, int64_t num_tokens, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, void* stream);
+
+/*
+ * Decode attention reads, for one query token per sequence, the whole
+ * context through the sequence's block table (P1, "第六站：注意力层"; the
+ * store runs first, so the context includes the current token).
+ *
+ * paged_attn_decode_workspace_size returns the bytes of device workspace
+ * paged_attn_decode needs for these sizes (fp32 partial results of the
+ * split-K pass). It depends only on its arguments; 0 is never returned for a
+ * non-empty problem.
+ */
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_context_len);
+
+/*
+ * paged_attn_decode — out[s, h] = softmax_j(scale * q[s,h] . K[j, g]) V[j, g]
+ * over the context positions j < context_lens[s], g = h / (num_q_heads /
+ * num_kv_heads) (consecutive query heads share a KV head).
+ *
+ *   out              device bf16 [num_seqs, num_q_heads, head_dim] (written)
+ *   q                device bf16 [num_seqs, num_q_heads, head_dim] contiguous
+ *   k_cache, v_cache device bf16 caches as for kv_store
+ *   block_tables     device int32 [num_seqs, block_table_stride]; entry j of
+ *                    row s holds the physical block of positions
+ *                    [j * 256, (j + 1) * 256)
+ *   context_lens     device int32 [num_seqs]; 0 marks a padding row, whose
+ *                    output is all zeros
+ *   max_context_len  host upper bound on context_lens (sizes the launch); a
+ *                    context longer than it is an error of the caller
+ *   scale            softmax scale (1/sqrt(head_dim) for the usual attention)
+ *   workspace        device memory of at least workspace_size bytes (256-byte
+ *                    aligned), owned by the caller, reusable across calls on
+ *                    one stream
+ * Supported: head_dim 128, block_size 256, num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8}, num_kv_heads <= 64.
+ * Results are deterministic (a fixed split plan; no atomics).
+ */
+pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t block_table_stride,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int64_t num_blocks, float scale, int32_t max_context_len,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_prefill_varlen — causal attention for a batch of variable-length
+ * query runs whose keys are read through block tables.
+ *
+ * Sequence s computes n_s = cu_seqlens_q[s+1] - cu_seqlens_q[s] query tokens,
+ * the last n_s of its context of L_s = context_lens[s] tokens, so its first
+ * c_s = L_s - n_s tokens are cached (a prefix hit or an earlier chunk; P1,
+ * "第二站：一个请求的状态" and "第三站：调度器"). Query i of sequence s sits at
+ * position c_s + i and attends keys 0 .. c_s + i (P1, "第六站：注意力层": with
+ * a prefix hit or a chunk continuation the whole context is read from the
+ * paged cache). K/V of the new tokens must already be stored (kv_store).
+ *
+ *   out              device bf16 [total_q, num_q_heads, head_dim] (written)
+ *   q                device bf16 [total_q, num_q_heads, head_dim] contiguous
+ *   cu_seqlens_q     device int32 [num_seqs + 1], cu[0] = 0, non-decreasing,
+ *                    cu[num_seqs] = total_q
+ *   context_lens     device int32 [num_seqs], L_s >= n_s
+ *   block_tables     device int32 [num_seqs, block_table_stride]
+ *   max_q_len        host upper bound on n_s (sizes the launch)
+ *   max_context_len  host upper bound on L_s
+ * Supported shapes as for paged_attn_decode. Deterministic.
+ */
+pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,
+                                     const int32_t* context_lens, const void* k_cache,
+                                     const void* v_cache, const int32_t* block_tables,
+                                     int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                                     int32_t max_q_len, int32_t max_context_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int64_t num_blocks, float scale,
+                                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

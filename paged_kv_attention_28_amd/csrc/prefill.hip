@@ -1,0 +1,343 @@
+// paged_attn_prefill_varlen: causal varlen attention whose queries start at
+// num_cached_tokens, keys read through the block table.
+//
+// P1 = "13. 读一个最小推理引擎：nano-vllm": the step computes only tokens from
+// num_cached onward ("第二站：一个请求的状态"); with a prefix hit or a chunk
+// continuation the whole context is read from the paged cache through the
+// block table ("第六站：注意力层"); only the first sequence of a step may be a
+// chunk cut at an arbitrary point ("第三站：调度器").
+//
+// gfx950 design (the two genuinely dense contractions run on MFMA):
+//  * Work-group = 4 wavefronts on 128 (token, head) rows of one sequence and
+//    one KV head: 128 / G query tokens x the G query heads sharing that KV
+//    head, so each K/V tile staged in LDS serves every one of them.
+//  * Grid (kv_head, seq, q-tile counted from the end). kv_head is fastest, so
+//    (with round-robin dispatch over the 8 XCDs) all tiles of one KV head
+//    land on one XCD and share its L2; the last (longest) q-tiles of every
+//    sequence are dispatched first.
+//  * Per 64-key tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows
+//    from LDS, B = the wavefront's 32 query rows held in registers). In the
+//    transposed product each lane holds 32 scores of one query row, so the
+//    row max and sum need a single cross-lane exchange (lane ^ 32).
+//  * O^T += V^T P^T, again 32x32x16: B = P taken straight from the S^T
+//    accumulators (rounded to bf16) because the K rows were fed to the first
+//    product in a permuted order (bits 2 and 3 of the row index swapped)
+//    that makes each lane's 8 scores belong to 8 consecutive keys; A = V^T
+//    from LDS, transposed while staging.
+//  * fp32 online softmax in the log2 domain; fully masked 32-key subtiles
+//    above the causal diagonal are skipped; K/V of tile i+1 are fetched from
+//    HBM into registers while tile i is computed; two LDS buffers, one
+//    barrier per tile.
+//  * Keys past the context end are clamped to the last context row (a valid,
+//    written row) and masked, so stale cache rows never enter the result.
+
+#include "common.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kKeysPerTile = 64;
+constexpr int kKStride = kHeadDim + 8;      // K tile row: 272 bytes (bank-conflict-free 16-byte reads)
+constexpr int kVStride = kKeysPerTile + 8;  // V^T tile row: 144 bytes
+constexpr int kKTileElems = kKeysPerTile * kKStride;
+constexpr int kVTileElems = kHeadDim * kVStride;
+constexpr int kBufElems = kKTileElems + kVTileElems;
+constexpr float kNegBig = -1e30f;
+
+__device__ __forceinline__ int perm_row(int m) {  // swap bits 2 and 3
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+struct TileRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+// Fetch K/V of keys [key0, key0 + 64) (clamped to the context) into registers.
+// K: thread t moves 16-byte chunk (t & 15) of keys (t >> 4) + 16 i.
+// V: thread t moves dims 8 (t & 15) .. +7 of keys 4 (t >> 4) .. +3.
+__device__ __forceinline__ void fetch_tile(TileRegs& r, const char* __restrict__ kc, const char* __restrict__ vc,
+                                           const int32_t* __restrict__ bt, int key0, int L, int hkv, int g,
+                                           int64_t num_blocks) {
+  int64_t blk = bt[key0 >> 8];
+  if (blk < 0 || blk >= num_blocks) blk = 0;  // caller error: stay inside the pool
+  const int t = threadIdx.x;
+  const int part = t & 15;
+  const int grp = t >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int key = key0 + grp + 16 * i;
+    key = key < L ? key : L - 1;
+    const int64_t row = (blk * kBlockSize + (key & (kBlockSize - 1))) * hkv + g;
+    r.k[i] = *reinterpret_cast<const u32x4*>(kc + row * (kHeadDim * 2) + part * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int key = key0 + 4 * grp + i;
+    key = key < L ? key : L - 1;
+    const int64_t row = (blk * kBlockSize + (key & (kBlockSize - 1))) * hkv + g;
+    r.v[i] = *reinterpret_cast<const u32x4*>(vc + row * (kHeadDim * 2) + part * 16);
+  }
+}
+
+__device__ __forceinline__ void stage_tile(const TileRegs& r, uint16_t* buf) {
+  const int t = threadIdx.x;
+  const int part = t & 15;
+  const int grp = t >> 4;
+  uint16_t* kt = buf;
+  uint16_t* vt = buf + kKTileElems;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(kt + (grp + 16 * i) * kKStride + part * 8) = r.k[i];
+  // transpose 4 keys x 8 dims into 8 rows (dims) of 4 keys
+  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[0]);
+  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[1]);
+  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[2]);
+  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[3]);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const int wi = d >> 1;
+    const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+    u32x2 pair;
+    pair.x = __builtin_amdgcn_perm(w1[wi], w0[wi], sel);
+    pair.y = __builtin_amdgcn_perm(w3[wi], w2[wi], sel);
+    *reinterpret_cast<u32x2*>(vt + (part * 8 + d) * kVStride + 4 * grp) = pair;
+  }
+}
+
+template <int G>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
+    const int32_t* __restrict__ context_lens, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, int bt_stride, int hq, int hkv, int64_t num_blocks,
+    float scale_log2, int max_q, int max_ctx) {
+  constexpr int kTokWG = 128 / G;  // query tokens per work-group
+  constexpr int kTokW = 32 / G;    // per wavefront
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBufElems];
+
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int zt = blockIdx.z;
+  const int q0 = cu_seqlens_q[b];
+  int n = cu_seqlens_q[b + 1] - q0;
+  n = n > max_q ? max_q : n;
+  int L = context_lens[b];
+  L = L > max_ctx ? max_ctx : L;
+  const int c = L - n;
+  if (n <= 0 || c < 0) return;
+  const int ntiles = (n + kTokWG - 1) / kTokWG;
+  if (zt >= ntiles) return;
+  const int tok_begin = (ntiles - 1 - zt) * kTokWG;
+  const int tok_end = tok_begin + kTokWG < n ? tok_begin + kTokWG : n;
+  const int kv_end = c + tok_end;
+  const int nkt = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 31;  // query row of this lane in the wavefront's 32 rows
+  const int half = lane >> 5;
+
+  // wavefront's rows and query positions
+  const int wtok0 = tok_begin + wave * kTokW;
+  const bool wave_live = wtok0 < tok_end;
+  const int wtok1 = wtok0 + kTokW < tok_end ? wtok0 + kTokW : tok_end;
+  const int pmin = c + wtok0;
+  const int pmax = c + wtok1 - 1;
+
+  const int r = wave * 32 + col;
+  const int tok = tok_begin + r / G;
+  const bool row_valid = tok < tok_end;
+  const int tokc = row_valid ? tok : tok_end - 1;
+  const int qhead = g * G + (r % G);
+  const int pos = c + tokc;
+
+  // query rows as the B operand of S^T = K Q^T: dims 16 kk + 8 half .. +7
+  u32x4 qreg[8];
+  {
+    const uint16_t* qp = q + ((int64_t)(q0 + tokc) * hq + qhead) * kHeadDim + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qreg[kk] = *reinterpret_cast<const u32x4*>(qp + 16 * kk);
+  }
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc_o[dt][i] = 0.f;
+  float m_run = kNegBig;
+  float l_run = 0.f;
+
+  const int32_t* bt = block_tables + (int64_t)b * bt_stride;
+  TileRegs regs;
+  fetch_tile(regs, k_cache, v_cache, bt, 0, L, hkv, g, num_blocks);
+  stage_tile(regs, smem);
+  __syncthreads();
+
+  const int krow = perm_row(col);  // K row fed to lane `col` of the A operand
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const bool has_next = kt + 1 < nkt;
+    if (has_next) fetch_tile(regs, k_cache, v_cache, bt, (kt + 1) * kKeysPerTile, L, hkv, g, num_blocks);
+    const uint16_t* kbuf = smem + (kt & 1) * kBufElems;
+    const uint16_t* vbuf = kbuf + kKTileElems;
+    const int key0 = kt * kKeysPerTile;
+    const bool act0 = wave_live && key0 <= pmax;
+    const bool act1 = wave_live && key0 + 32 <= pmax;
+    if (act0) {
+      f32x16 s[2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+        if (st == 1 && !act1) continue;
+        const uint16_t* kr = kbuf + (32 * st + krow) * kKStride + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kr + 16 * kk);
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[st], 0, 0, 0);
+        }
+      }
+      // mask: key index of accumulator element i of subtile st
+      const bool need_mask = key0 + kKeysPerTile - 1 > pmin;
+      float mx = kNegBig;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = 8 * (i >> 2) + 4 * half + (i & 3);
+          const int key = key0 + 32 * st + perm_row(m);
+          float x = s[st][i];
+          if ((st == 1 && !act1) || (need_mask && key > pos)) x = -__builtin_inff();
+          s[st][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx * scale_log2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      float lsum = 0.f;
+      u32x4 pk[2][2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        float p[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][i], scale_log2, -m_new));
+          lsum += p[i];
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          pk[st][qq].x = pack_bf16x2(p[8 * qq + 0], p[8 * qq + 1]);
+          pk[st][qq].y = pack_bf16x2(p[8 * qq + 2], p[8 * qq + 3]);
+          pk[st][qq].z = pack_bf16x2(p[8 * qq + 4], p[8 * qq + 5]);
+          pk[st][qq].w = pack_bf16x2(p[8 * qq + 6], p[8 * qq + 7]);
+        }
+      }
+      l_run = l_run * alpha + lsum;
+      m_run = m_new;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_o[dt][i] *= alpha;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint16_t* vr = vbuf + (dt * 32 + col) * kVStride + 8 * half;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          if (st == 1 && !act1) continue;
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(vr + 32 * st + 16 * qq);
+            acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pk[st][qq]), acc_o[dt],
+                                                                0, 0, 0);
+          }
+        }
+      }
+    }
+    if (has_next) stage_tile(regs, smem + ((kt + 1) & 1) * kBufElems);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds O^T[dims dt*32 + 8 (i/4) + 4 half + (i%4)][its query row]
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (row_valid && wave_live) {
+    const float inv = 1.f / l_tot;
+    uint16_t* op = out + ((int64_t)(q0 + tok) * hq + qhead) * kHeadDim + 4 * half;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 w;
+        w.x = pack_bf16x2(acc_o[dt][4 * rq + 0] * inv, acc_o[dt][4 * rq + 1] * inv);
+        w.y = pack_bf16x2(acc_o[dt][4 * rq + 2] * inv, acc_o[dt][4 * rq + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * rq) = w;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+}  // namespace pkv
+
+extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,
+                                                const int32_t* context_lens, const void* k_cache,
+                                                const void* v_cache, const int32_t* block_tables,
+                                                int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                                                int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                int64_t num_blocks, float scale, void* stream) {
+  using namespace pkv;
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0 || num_blocks < 0 ||
+      block_table_stride < 0)
+    return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: negative size");
+  if (head_dim != kHeadDim)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: head_dim %d (128 only)", head_dim);
+  if (block_size != kBlockSize)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: block_size %d (256 only)", block_size);
+  if (num_kv_heads < 1 || num_kv_heads > 64 || num_q_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: head counts %d/%d unsupported", num_q_heads,
+                num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: %d query heads per KV head (1, 2, 4 or 8)", G);
+  if (!(scale > 0.f) || !__builtin_isfinite(scale))
+    return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: scale must be finite and > 0");
+  if (max_q_len > max_context_len)
+    return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: max_q_len > max_context_len");
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_tables)
+    return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: null pointer");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: q, out and caches must be 16-byte aligned");
+  const int64_t need_bt = (max_context_len + kBlockSize - 1) / kBlockSize;
+  if (block_table_stride < need_bt)
+    return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: block_table_stride %d < %lld", block_table_stride,
+                (long long)need_bt);
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: more than 65535 sequences");
+  const int tok_wg = 128 / G;
+  const int ztiles = (max_q_len + tok_wg - 1) / tok_wg;
+  if (ztiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: max_q_len too large");
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  dim3 grid(num_kv_heads, num_seqs, ztiles);
+  uint16_t* o = static_cast<uint16_t*>(out);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const char* kc = static_cast<const char*>(k_cache);
+  const char* vc = static_cast<const char*>(v_cache);
+#define PKV_PREFILL_LAUNCH(GG)                                                                                  \
+  hipLaunchKernelGGL(prefill_kernel<GG>, grid, dim3(256), 0, s, o, qq, cu_seqlens_q, context_lens, kc, vc,      \
+                     block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2,      \
+                     max_q_len, max_context_len)
+  switch (G) {
+    case 1: PKV_PREFILL_LAUNCH(1); break;
+    case 2: PKV_PREFILL_LAUNCH(2); break;
+    case 4: PKV_PREFILL_LAUNCH(4); break;
+    default: PKV_PREFILL_LAUNCH(8); break;
+  }
+#undef PKV_PREFILL_LAUNCH
+  return check_launch("paged_attn_prefill_varlen");
+}

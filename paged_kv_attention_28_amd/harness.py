@@ -1,0 +1,168 @@
+"""Runs a synthetic workload on the GPU through the C ABI.
+
+Used by the GPU tests, ``bench.py`` and the smoke check. It only moves data
+and calls ``binding``: step metadata comes from the library's own
+``pkv_prepare_step`` and every device computation from its kernels. Random
+values come from the shared seeded generator in ``workloads``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads as W
+
+from . import binding as B
+
+NAN_BF16 = 0x7FC0  # quiet NaN bit pattern used to poison unwritten cache rows
+
+
+def poisoned_cache(w: W.Workload, device="cuda") -> torch.Tensor:
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    t.view(torch.int16).fill_(NAN_BF16)
+    return t
+
+
+def meta(w: W.Workload, batch: W.Batch, out=None) -> B.StepMeta:
+    return B.pkv_prepare_step([s.seq_len for s in batch.seqs], [s.num_cached for s in batch.seqs],
+                              [s.block_table for s in batch.seqs], w.block_size, w.max_blocks_per_seq,
+                              batch.num_pad, out=out)
+
+
+class DeviceMeta:
+    """Device copies of one batch's metadata."""
+
+    def __init__(self, m: B.StepMeta, device="cuda"):
+        self.host = m
+        self.slot_mapping = torch.from_numpy(np.ascontiguousarray(m.slot_mapping)).to(device)
+        self.cu_seqlens_q = torch.from_numpy(np.ascontiguousarray(m.cu_seqlens_q)).to(device)
+        self.context_lens = torch.from_numpy(np.ascontiguousarray(m.context_lens)).to(device)
+        self.block_tables = torch.from_numpy(np.ascontiguousarray(m.block_tables)).to(device)
+        self.max_q_len = m.max_q_len
+        self.max_context_len = m.max_context_len
+        self.num_tokens = m.num_tokens
+
+
+class DeviceWorkload:
+    """Poisoned caches, setup stores, the step's store and attention passes."""
+
+    def __init__(self, w: W.Workload, device="cuda"):
+        self.w = w
+        self.device = device
+        self.k_cache = poisoned_cache(w, device)
+        self.v_cache = poisoned_cache(w, device)
+
+    # -- stores --------------------------------------------------------------
+    def run_setup(self):
+        for b in self.w.setup:
+            k, v = W.batch_kv(self.w, b, self.device)
+            m = DeviceMeta(meta(self.w, b), self.device)
+            B.kv_store(k, v, self.k_cache, self.v_cache, m.slot_mapping)
+
+    def store_slots(self) -> torch.Tensor:
+        slots = meta(self.w, self.w.store).slot_mapping
+        mask = W.real_row_mask(self.w)
+        full = np.full(mask.size, -1, dtype=np.int32)
+        full[mask] = slots
+        return torch.from_numpy(full).to(self.device)
+
+    def run_store(self):
+        k, v = W.store_kv(self.w, self.device)
+        B.kv_store(k, v, self.k_cache, self.v_cache, self.store_slots())
+
+    def build(self):
+        self.run_setup()
+        self.run_store()
+        return self
+
+    # -- attention -----------------------------------------------------------
+    def pass_inputs(self, p: W.Pass):
+        q = W.pass_q(self.w, p, self.device)
+        return q, DeviceMeta(meta(self.w, p.batch), self.device)
+
+    def run_pass(self, p: W.Pass, q=None, m: DeviceMeta = None, out=None, workspace=None):
+        if q is None or m is None:
+            q, m = self.pass_inputs(p)
+        if out is None:
+            out = torch.empty_like(q)
+        if p.kind == "decode":
+            if workspace is None:
+                workspace = decode_workspace(self.w, q.shape[0], m.max_context_len, self.device)
+            B.paged_attn_decode(out, q, self.k_cache, self.v_cache, m.block_tables, m.context_lens, self.w.scale,
+                                m.max_context_len, workspace)
+        else:
+            B.paged_attn_prefill_varlen(out, q, m.cu_seqlens_q, m.context_lens, self.k_cache, self.v_cache,
+                                        m.block_tables, m.max_q_len, m.max_context_len, self.w.scale)
+        return out
+
+
+def decode_workspace(w: W.Workload, num_seqs: int, max_ctx: int, device="cuda") -> torch.Tensor:
+    n = B.paged_attn_decode_workspace_size(num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_ctx)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+class StepRunner:
+    """One engine step of a single-pass workload, as an engine runs it:
+    host step preparation into pinned buffers, asynchronous upload of the
+    metadata, the store of the step's K/V, then the attention pass.
+
+    Two pinned buffer sets alternate, so the host may prepare step i + 1
+    while step i is still on the GPU; an event guards each set's reuse."""
+
+    def __init__(self, dw: DeviceWorkload, p: W.Pass):
+        self.dw, self.p, w = dw, p, dw.w
+        dev = dw.device
+        self.q = W.pass_q(w, p, dev)
+        self.k, self.v = W.store_kv(w, dev)
+        self.out = torch.empty_like(self.q)
+        m0 = meta(w, p.batch)
+        rows = len(p.batch.seqs) + p.batch.num_pad
+        self.shapes = (m0.num_tokens, rows + 1, rows, rows * w.max_blocks_per_seq)
+        self.pinned = []
+        for _ in range(2):
+            self.pinned.append(tuple(torch.empty(n, dtype=torch.int32).pin_memory() for n in self.shapes))
+        self.events = [None, None]
+        self.dev_meta = tuple(torch.empty(n, dtype=torch.int32, device=dev) for n in self.shapes)
+        self.max_q_len = m0.max_q_len
+        self.max_ctx = m0.max_context_len
+        self.workspace = (decode_workspace(w, rows, self.max_ctx, dev) if p.kind == "decode" else None)
+        self.i = 0
+
+    def prepare_and_upload(self):
+        w, p = self.dw.w, self.p
+        k = self.i & 1
+        self.i += 1
+        if self.events[k] is not None:
+            self.events[k].synchronize()
+        bufs = self.pinned[k]
+        meta(w, p.batch, out=tuple(b.numpy() for b in bufs))
+        for d, h in zip(self.dev_meta, bufs):
+            d.copy_(h, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record()
+        self.events[k] = ev
+
+    def store_only(self):
+        slots = self.dev_meta[0]
+        B.kv_store(self.k, self.v, self.dw.k_cache, self.dw.v_cache, slots)
+
+    def attention_only(self):
+        w = self.dw.w
+        _, cu, ctx, bt = self.dev_meta
+        bt2 = bt.view(-1, w.max_blocks_per_seq)
+        if self.p.kind == "decode":
+            B.paged_attn_decode(self.out, self.q, self.dw.k_cache, self.dw.v_cache, bt2, ctx, w.scale,
+                                self.max_ctx, self.workspace)
+        else:
+            B.paged_attn_prefill_varlen(self.out, self.q, cu, ctx, self.dw.k_cache, self.dw.v_cache, bt2,
+                                        self.max_q_len, self.max_ctx, w.scale)
+
+    def kernels(self):
+        self.store_only()
+        self.attention_only()
+
+    def step(self):
+        self.prepare_and_upload()
+        self.kernels()

@@ -44,9 +44,14 @@ def empty_caches(w: W.Workload):
 def build_caches(w: W.Workload, device="cpu"):
     """Poisoned caches after the setup stores and the step's store."""
     kc, vc = empty_caches(w)
-    for b in w.setup:
-        k, v = W.batch_kv(w, b, device)
-        kc, vc = op.kv_store_ref(kc, vc, bits(k), bits(v), metadata(w, b)[0])
+    if w.setup:
+        # setup batches write disjoint slots (the oracle's store rejects
+        # duplicates), so they are applied as one store
+        ks, vs, ss = [], [], []
+        for b in w.setup:
+            k, v = W.batch_kv(w, b, device)
+            ks.append(bits(k)); vs.append(bits(v)); ss.append(metadata(w, b)[0])
+        kc, vc = op.kv_store_ref(kc, vc, np.concatenate(ks), np.concatenate(vs), np.concatenate(ss))
     k, v = W.store_kv(w, device)
     kc, vc = op.kv_store_ref(kc, vc, bits(k), bits(v), store_slots(w))
     return kc, vc
