@@ -31,15 +31,22 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 round-to-nearest-even (NaN kept quiet), as a 16-bit pattern.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN): one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Makes the compiler wait here until `v` has arrived (an empty asm that reads
+// it). Used once, before a loop, on registers loaded ahead of the loop, so
+// that the waits the compiler places inside the loop only have to cover the
+// loads issued in the loop itself.
+__device__ __forceinline__ void retire(const u32x4& v) { asm volatile("" ::"v"(v)); }
 
 }  // namespace pkv

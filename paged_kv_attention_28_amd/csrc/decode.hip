@@ -185,28 +185,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int t1 = t0 + split < L ? t0 + split : L;
     const int nstep = (t1 - t0 + 63) >> 6;  // 64 tokens per work-group step
     const int32_t* bt = block_tables + (int64_t)b * bt_stride;
+    // a block id outside the pool is a caller error: read block 0 instead
+    // (stays inside the cache; the result is unspecified)
+    auto block_of = [&](int base) -> int64_t {
+      const int64_t blk = bt[base >> 8];
+      return (blk >= 0 && blk < num_blocks) ? blk : 0;
+    };
     Step A, B;
-    int64_t blkA = bt[t0 >> 8];
-    bool okA = blkA >= 0 && blkA < num_blocks;
-    if (okA) load_step(A, k_cache, v_cache, blkA, t0, wave, grp, li, t1, hkv, g);
+    load_step(A, k_cache, v_cache, block_of(t0), t0, wave, grp, li, t1, hkv, g);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      retire(qa[h]);
+      retire(qb[h]);
+    }
+    // Loads of the next step are issued unconditionally (the last one
+    // re-reads the final step, an L2 hit) so that no wait is merged across
+    // a conditional load.
+    const int last = t0 + (nstep - 1) * 64;
     for (int it = 0; it < nstep; it += 2) {
       const int baseA = t0 + it * 64;
-      const int baseB = baseA + 64;
-      const bool hasB = it + 1 < nstep;
-      int64_t blkB = 0;
-      bool okB = false;
-      if (hasB) {
-        blkB = bt[baseB >> 8];
-        okB = blkB >= 0 && blkB < num_blocks;
-        if (okB) load_step(B, k_cache, v_cache, blkB, baseB, wave, grp, li, t1, hkv, g);
-      }
-      if (okA) compute_step<G>(S, A, qa, qb, baseA, wave, grp, t1, scale_log2);
-      if (it + 2 < nstep) {
-        blkA = bt[(baseA + 128) >> 8];
-        okA = blkA >= 0 && blkA < num_blocks;
-        if (okA) load_step(A, k_cache, v_cache, blkA, baseA + 128, wave, grp, li, t1, hkv, g);
-      }
-      if (hasB && okB) compute_step<G>(S, B, qa, qb, baseB, wave, grp, t1, scale_log2);
+      const int baseB = baseA + 64 < last ? baseA + 64 : last;
+      const int baseN = baseA + 128 < last ? baseA + 128 : last;
+      load_step(B, k_cache, v_cache, block_of(baseB), baseB, wave, grp, li, t1, hkv, g);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      compute_step<G>(S, A, qa, qb, baseA, wave, grp, t1, scale_log2);
+      load_step(A, k_cache, v_cache, block_of(baseN), baseN, wave, grp, li, t1, hkv, g);
+      __builtin_amdgcn_sched_barrier(0);
+      // unconditional so that B's loads stay ahead of compute(A); a step past
+      // the split end (odd step counts only) is fully masked
+      compute_step<G>(S, B, qa, qb, baseA + 64, wave, grp, it + 1 < nstep ? t1 : 0, scale_log2);
     }
   }
 

@@ -22,9 +22,12 @@
 //  * O^T += V^T P^T, again 32x32x16: B = P taken straight from the S^T
 //    accumulators (rounded to bf16) because the K rows were fed to the first
 //    product in a permuted order (bits 2 and 3 of the row index swapped)
-//    that makes each lane's 8 scores belong to 8 consecutive keys; A = V^T
-//    from LDS, transposed while staging.
-//  * fp32 online softmax in the log2 domain; fully masked 32-key subtiles
+//    that makes each lane's 8 scores belong to 8 consecutive keys; A = V^T,
+//    read from the row-major V tile with gfx950's transposing LDS load
+//    (ds_read_b64_tr_b16), so V is staged exactly like K.
+//  * fp32 online softmax in the log2 domain with lazy rescaling (the
+//    reference max moves only when a row max exceeds it by 8, so most tiles
+//    skip rescaling the 64 output accumulators); fully masked 32-key subtiles
 //    above the causal diagonal are skipped; K/V of tile i+1 are fetched from
 //    HBM into registers while tile i is computed; two LDS buffers, one
 //    barrier per tile.
@@ -38,12 +41,16 @@ namespace pkv {
 namespace {
 
 constexpr int kKeysPerTile = 64;
-constexpr int kKStride = kHeadDim + 8;      // K tile row: 272 bytes (bank-conflict-free 16-byte reads)
-constexpr int kVStride = kKeysPerTile + 8;  // V^T tile row: 144 bytes
-constexpr int kKTileElems = kKeysPerTile * kKStride;
-constexpr int kVTileElems = kHeadDim * kVStride;
+constexpr int kKPitch = kHeadDim + 8;   // K tile row: 272 B; 16-byte reads of 16 rows hit 64 distinct banks
+constexpr int kVPitch = kHeadDim + 32;  // V tile row: 320 B; transposing 8-byte reads of 2x4 rows hit distinct banks
+constexpr int kKTileElems = kKeysPerTile * kKPitch;
+constexpr int kVTileElems = kKeysPerTile * kVPitch;
 constexpr int kBufElems = kKTileElems + kVTileElems;
 constexpr float kNegBig = -1e30f;
+constexpr float kRescaleSlack = 8.f;  // log2 units: the reference max moves only when a row max exceeds it by this
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ int perm_row(int m) {  // swap bits 2 and 3
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
@@ -51,59 +58,61 @@ __device__ __forceinline__ int perm_row(int m) {  // swap bits 2 and 3
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4k + c names row k, 4-element chunk c; lane i receives element i of the
+// group's 4 x 16 block from rows 0..3.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+#pragma clang diagnostic pop
+  return __builtin_bit_cast(uint2, v);
+}
+
 struct TileRegs {
   u32x4 k[4];
   u32x4 v[4];
 };
 
-// Fetch K/V of keys [key0, key0 + 64) (clamped to the context) into registers.
-// K: thread t moves 16-byte chunk (t & 15) of keys (t >> 4) + 16 i.
-// V: thread t moves dims 8 (t & 15) .. +7 of keys 4 (t >> 4) .. +3.
+// K and V of keys [key0, key0 + 64) into registers; both caches share the
+// layout, so one set of offsets serves both. Thread t moves 16-byte chunk
+// (t & 15) of keys (t >> 4) + 16 i; keys past the context end are clamped
+// to its last row.
 __device__ __forceinline__ void fetch_tile(TileRegs& r, const char* __restrict__ kc, const char* __restrict__ vc,
-                                           const int32_t* __restrict__ bt, int key0, int L, int hkv, int g,
-                                           int64_t num_blocks) {
+                                           const int32_t* __restrict__ bt, int key0, int L, int64_t row_bytes,
+                                           int64_t block_bytes, int64_t thread_off, int64_t num_blocks) {
   int64_t blk = bt[key0 >> 8];
   if (blk < 0 || blk >= num_blocks) blk = 0;  // caller error: stay inside the pool
-  const int t = threadIdx.x;
-  const int part = t & 15;
-  const int grp = t >> 4;
+  const int64_t base = blk * block_bytes + (int64_t)(key0 & (kBlockSize - 1)) * row_bytes + thread_off;
+  const int local = threadIdx.x >> 4;
+  if (key0 + kKeysPerTile <= L) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int key = key0 + grp + 16 * i;
-    key = key < L ? key : L - 1;
-    const int64_t row = (blk * kBlockSize + (key & (kBlockSize - 1))) * hkv + g;
-    r.k[i] = *reinterpret_cast<const u32x4*>(kc + row * (kHeadDim * 2) + part * 16);
-  }
+    for (int i = 0; i < 4; ++i) {
+      r.k[i] = *reinterpret_cast<const u32x4*>(kc + base + 16 * i * row_bytes);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vc + base + 16 * i * row_bytes);
+    }
+  } else {
+    const int last = L - 1 - key0;  // >= 0: the tile starts inside the context
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int key = key0 + 4 * grp + i;
-    key = key < L ? key : L - 1;
-    const int64_t row = (blk * kBlockSize + (key & (kBlockSize - 1))) * hkv + g;
-    r.v[i] = *reinterpret_cast<const u32x4*>(vc + row * (kHeadDim * 2) + part * 16);
+    for (int i = 0; i < 4; ++i) {
+      const int kl = local + 16 * i;
+      const int64_t off = base + (int64_t)((kl < last ? kl : last) - local) * row_bytes;
+      r.k[i] = *reinterpret_cast<const u32x4*>(kc + off);
+      r.v[i] = *reinterpret_cast<const u32x4*>(vc + off);
+    }
   }
 }
 
 __device__ __forceinline__ void stage_tile(const TileRegs& r, uint16_t* buf) {
   const int t = threadIdx.x;
   const int part = t & 15;
-  const int grp = t >> 4;
+  const int local = t >> 4;
   uint16_t* kt = buf;
   uint16_t* vt = buf + kKTileElems;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(kt + (grp + 16 * i) * kKStride + part * 8) = r.k[i];
-  // transpose 4 keys x 8 dims into 8 rows (dims) of 4 keys
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.v[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.v[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.v[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.v[3]);
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    const int wi = d >> 1;
-    const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-    u32x2 pair;
-    pair.x = __builtin_amdgcn_perm(w1[wi], w0[wi], sel);
-    pair.y = __builtin_amdgcn_perm(w3[wi], w2[wi], sel);
-    *reinterpret_cast<u32x2*>(vt + (part * 8 + d) * kVStride + 4 * grp) = pair;
+  for (int i = 0; i < 4; ++i) {
+    *reinterpret_cast<u32x4*>(kt + (local + 16 * i) * kKPitch + part * 8) = r.k[i];
+    *reinterpret_cast<u32x4*>(vt + (local + 16 * i) * kVPitch + part * 8) = r.v[i];
   }
 }
 
@@ -166,20 +175,32 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc_o[dt][i] = 0.f;
-  float m_run = kNegBig;
+  float m_ref = kNegBig;  // reference max (log2 domain) of this lane's row
   float l_run = 0.f;
 
+  const int64_t row_bytes = (int64_t)hkv * kHeadDim * 2;
+  const int64_t block_bytes = row_bytes * kBlockSize;
+  const int64_t thread_off = (int64_t)(threadIdx.x >> 4) * row_bytes + (int64_t)g * kHeadDim * 2 + (threadIdx.x & 15) * 16;
   const int32_t* bt = block_tables + (int64_t)b * bt_stride;
   TileRegs regs;
-  fetch_tile(regs, k_cache, v_cache, bt, 0, L, hkv, g, num_blocks);
+  fetch_tile(regs, k_cache, v_cache, bt, 0, L, row_bytes, block_bytes, thread_off, num_blocks);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) retire(qreg[kk]);
   stage_tile(regs, smem);
   __syncthreads();
 
-  const int krow = perm_row(col);  // K row fed to lane `col` of the A operand
+  // per-lane LDS offsets (elements)
+  const int k_rd = perm_row(col) * kKPitch + 8 * half;  // A operand of S^T: K row perm_row(col)
+  // A operand of O^T: V^T via transposing reads; lane group q16 = lane / 16
+  const int q16 = lane >> 4;
+  const int v_rd = (8 * (q16 >> 1) + ((lane & 15) >> 2)) * kVPitch + 16 * (q16 & 1) + 4 * (lane & 3);
 
   for (int kt = 0; kt < nkt; ++kt) {
     const bool has_next = kt + 1 < nkt;
-    if (has_next) fetch_tile(regs, k_cache, v_cache, bt, (kt + 1) * kKeysPerTile, L, hkv, g, num_blocks);
+    if (has_next)
+      fetch_tile(regs, k_cache, v_cache, bt, (kt + 1) * kKeysPerTile, L, row_bytes, block_bytes, thread_off,
+                 num_blocks);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
     const uint16_t* kbuf = smem + (kt & 1) * kBufElems;
     const uint16_t* vbuf = kbuf + kKTileElems;
     const int key0 = kt * kKeysPerTile;
@@ -189,34 +210,53 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       f32x16 s[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
+        if (st == 1 && !act1) break;
+        const uint16_t* kr = kbuf + 32 * st * kKPitch + k_rd;
+        u32x4 a = *reinterpret_cast<const u32x4*>(kr);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[0]), f32x16{}, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-        if (st == 1 && !act1) continue;
-        const uint16_t* kr = kbuf + (32 * st + krow) * kKStride + 8 * half;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(kr + 16 * kk);
+        for (int kk = 1; kk < 8; ++kk) {
+          a = *reinterpret_cast<const u32x4*>(kr + 16 * kk);
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[st], 0, 0, 0);
         }
       }
-      // mask: key index of accumulator element i of subtile st
-      const bool need_mask = key0 + kKeysPerTile - 1 > pmin;
+      if (!act1) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[1][i] = -__builtin_inff();
+      }
+      // Accumulator element i of subtile st holds key
+      //   key0 + 32 st + 16 (i >> 3) + 8 half + (i & 7)
+      // (output row 8 (i/4) + 4 half + i%4 of the MFMA, through perm_row).
+      if (key0 + kKeysPerTile - 1 > pmin) {  // tile crosses the causal diagonal of some row
+        const int lim = pos - key0 - 8 * half;  // element visible iff its key offset <= lim
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * st + 16 * (i >> 3) + (i & 7) > lim) s[st][i] = -__builtin_inff();
+      }
       float mx = kNegBig;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = 8 * (i >> 2) + 4 * half + (i & 3);
-          const int key = key0 + 32 * st + perm_row(m);
-          float x = s[st][i];
-          if ((st == 1 && !act1) || (need_mask && key > pos)) x = -__builtin_inff();
-          s[st][i] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+      // Lazy rescale: exponents are taken against m_ref, which moves (and
+      // rescales this row's running sums) only when the row max exceeds it
+      // by more than kRescaleSlack, so weights stay <= 2^slack. The decision
+      // is per row (other rows keep alpha = 1 exactly), so a row's result
+      // never depends on the other rows of the wavefront.
+      const bool grow = mx > m_ref + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc_o[dt][i] *= alpha;
+        m_ref = m_new;
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       float lsum = 0.f;
       u32x4 pk[2][2];
 #pragma unroll
@@ -224,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         float p[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][i], scale_log2, -m_new));
+          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][i], scale_log2, -m_ref));
           lsum += p[i];
         }
 #pragma unroll
@@ -235,22 +275,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           pk[st][qq].w = pack_bf16x2(p[8 * qq + 6], p[8 * qq + 7]);
         }
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      l_run += lsum;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[dt][i] *= alpha;
-      }
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vr = vbuf + (dt * 32 + col) * kVStride + 8 * half;
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          if (st == 1 && !act1) continue;
+          if (st == 1 && !act1) break;
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(vr + 32 * st + 16 * qq);
+            const uint16_t* vr = vbuf + (32 * st + 16 * qq) * kVPitch + v_rd + 32 * dt;
+            const uint2 lo = lds_read_tr16(vr);
+            const uint2 hi = lds_read_tr16(vr + 4 * kVPitch);
+            const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
             acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pk[st][qq]), acc_o[dt],
                                                                 0, 0, 0);
           }
