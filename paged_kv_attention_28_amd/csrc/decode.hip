@@ -1,34 +1,41 @@
 // paged_attn_decode: one query token per sequence, context read through the
-// block table, split-K over the context plus a cross-split merge.
+// block table; a persistent stream-K pass over all context rows plus a merge
+// of the sequences that were split between wavefronts.
 //
 // P1 = "13. 读一个最小推理引擎：nano-vllm", section "第六站：注意力层": decode
 // attends its whole history, read from the paged cache through the block
 // table; the store runs first, so the context includes the current token.
 //
-// gfx950 design (HBM-bound: each K/V byte is read once, ~2 flop per byte):
-//  * Grid (kv_head, split, seq). kv_head is the fastest index, so the
-//    work-groups of all KV heads of one token range are dispatched together
-//    and sweep the same 2 KiB token rows of the cache at the same time.
-//  * One work-group = 4 wavefronts on one (seq, kv_head, split of `split`
-//    tokens). The G = H_q / H_kv query heads of the group are computed
-//    together, so every K/V byte fetched serves all G heads from registers.
-//  * A wavefront handles 16 tokens per step: 8 lane groups of 8 lanes, one
-//    token per group, each lane owning 32 bytes of the 256-byte head row
-//    (dims 8i..8i+7 and 64+8i..64+8i+7, so every 16-byte load instruction
-//    reads 128 contiguous bytes per token). q.k uses the bf16 dot2
-//    instruction, then a 3-step DPP sum inside the group.
-//  * Each lane group keeps its own fp32 online-softmax state (running max in
-//    the log2 domain, sum, 16 x G output accumulators); the 32 states of the
-//    work-group are combined once at the end (DPP/bpermute inside the
-//    wavefront, LDS across the 4 wavefronts).
-//  * Loads of the next 16-token step are issued before the current step is
-//    computed (two register buffers).
-//  * Masked positions (past the split end) load a valid row of the same
-//    split and get a score of -inf, so no stale or poisoned cache row is
-//    ever multiplied into the result.
-//  * A sequence with a single split writes its normalised bf16 output
-//    directly; otherwise the split writes (m, l, o) partials and the merge
-//    kernel combines them (log-sum-exp in the log2 domain).
+// gfx950 design (HBM-bound: every K/V byte is read once, ~2 flop per byte):
+//  * One wavefront reads whole token rows: a K (or V) row of one token is
+//    H_kv x 256 bytes; the 8 lane groups of 8 lanes cover 2 KiB, so every
+//    16-byte load instruction reads 1 KiB of contiguous cache. Lane group j
+//    serves KV head j % H_kv (and, when H_kv < 8, token j / H_kv of the
+//    window); each lane owns 32 bytes of the head row (dims 8i..8i+7 and
+//    64+8i..64+8i+7). The G query heads of the KV head are computed from the
+//    same registers.
+//  * q.k uses the bf16 dot2 instruction and a 3-step DPP sum inside the lane
+//    group; softmax is fp32 online softmax in the log2 domain per lane group.
+//  * Work split (stream-K): the context of every sequence is cut into steps
+//    of 2 windows (2 tokens for H_kv = 8). Each work-group first scans the
+//    context lengths in LDS; the global step list (sequence-major) is then
+//    divided evenly over all resident wavefronts of a persistent grid, so
+//    there are no empty work-groups and no tail of unequal splits. A
+//    wavefront walks its range across sequence boundaries with the loads of
+//    the next step always in flight (two register buffers; block-table rows
+//    and the next sequence's queries are prefetched). K/V loads are
+//    nontemporal: the rows are read once.
+//  * A wavefront that owns a whole sequence writes the normalised bf16
+//    output. A sequence cut between wavefronts leaves one fp32 (m, l, o)
+//    partial per piece, in slot 0 (piece starts the wavefront's range) or
+//    slot 1 (piece ends it) of that wavefront; the merge kernel finds the
+//    pieces from the same step arithmetic and combines them (log-sum-exp in
+//    the log2 domain), and writes zeros for padding rows (context 0).
+//  * Positions past the context end load the last context row (always
+//    written) and get a score of -inf: stale or poisoned cache rows never
+//    enter the result.
+
+#include <mutex>
 
 #include "common.h"
 
@@ -37,6 +44,9 @@ namespace pkv {
 namespace {
 
 constexpr float kNegBig = -1e30f;  // running-max start: finite, so m - m_new never forms inf - inf
+constexpr int kWavesCap = 4096;    // persistent grid cap (partial slots are sized for it)
+constexpr int kMinStepsPerWave = 16;
+constexpr int kMaxSeqs = 8192;     // LDS scan capacity
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -45,7 +55,6 @@ __device__ __forceinline__ float dpp(float x) {
 constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;  // row_half_mirror: lane i <- lane 7-i within 8
-constexpr int kRowRor8 = 0x128;     // row_ror:8 within 16 lanes
 
 // Sum over the 8 lanes of a lane group.
 __device__ __forceinline__ float group8_sum(float x) {
@@ -72,8 +81,8 @@ __device__ __forceinline__ float dot16(const u32x4& qa, const u32x4& qb, const u
   return s;
 }
 
-struct Step {
-  u32x4 k[2][2];  // [token t][half]
+struct Buf {
+  u32x4 k[2][2];  // [window t][half]
   u32x4 v[2][2];
 };
 
@@ -84,35 +93,45 @@ struct State {
   float o[G][16];
 };
 
-__device__ __forceinline__ void load_step(Step& st, const char* __restrict__ kc, const char* __restrict__ vc,
-                                          int64_t blk, int base, int wave, int grp, int li, int t_end, int hkv,
-                                          int g) {
+// Everything a step needs; wave-uniform.
+struct Step {
+  int b;                   // sequence
+  int s;                   // step index inside the sequence
+  int64_t row0;            // cache row of the step's first token
+  int last_valid_row_off;  // context length - 1 - first token of the step (>= 0)
+  bool live;               // false for a padding step past the wavefront's range (fully masked)
+};
+
+template <int HKV>
+__device__ __forceinline__ void load_buf(Buf& x, const char* __restrict__ kc, const char* __restrict__ vc,
+                                         const Step& st, int grp, int li) {
+  constexpr int TW = 8 / HKV;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    int tok = base + 16 * wave + 8 * t + grp;
-    tok = tok < t_end ? tok : t_end - 1;
-    const int64_t row = (blk * kBlockSize + (tok & (kBlockSize - 1))) * hkv + g;
+    int off = t * TW + grp / HKV;
+    off = off < st.last_valid_row_off ? off : st.last_valid_row_off;
+    const int64_t row = (st.row0 + off) * HKV + (grp % HKV);
     const char* kp = kc + row * (kHeadDim * 2) + li * 16;
     const char* vp = vc + row * (kHeadDim * 2) + li * 16;
-    st.k[t][0] = *reinterpret_cast<const u32x4*>(kp);
-    st.k[t][1] = *reinterpret_cast<const u32x4*>(kp + 128);
-    st.v[t][0] = *reinterpret_cast<const u32x4*>(vp);
-    st.v[t][1] = *reinterpret_cast<const u32x4*>(vp + 128);
+    x.k[t][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
+    x.k[t][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 128));
+    x.v[t][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
+    x.v[t][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 128));
   }
 }
 
-template <int G>
-__device__ __forceinline__ void compute_step(State<G>& S, const Step& st, const u32x4 (&qa)[G],
-                                             const u32x4 (&qb)[G], int base, int wave, int grp, int t_end,
-                                             float scale_log2) {
-  float s[2][G];
+template <int G, int HKV>
+__device__ __forceinline__ void compute_buf(State<G>& S, const Buf& x, const u32x4 (&qa)[G], const u32x4 (&qb)[G],
+                                            const Step& st, int grp, float scale_log2) {
+  constexpr int TW = 8 / HKV;
+  float sc[2][G];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const bool valid = base + 16 * wave + 8 * t + grp < t_end;
+    const bool valid = st.live && (t * TW + grp / HKV) <= st.last_valid_row_off;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float x = group8_sum(dot16(qa[h], qb[h], st.k[t][0], st.k[t][1]));
-      s[t][h] = valid ? x * scale_log2 : -__builtin_inff();
+      const float d = group8_sum(dot16(qa[h], qb[h], x.k[t][0], x.k[t][1]));
+      sc[t][h] = valid ? d * scale_log2 : -__builtin_inff();
     }
   }
   float vf[2][16];
@@ -120,7 +139,7 @@ __device__ __forceinline__ void compute_step(State<G>& S, const Step& st, const 
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const u32x4& w = st.v[t][half];
+      const u32x4& w = x.v[t][half];
       vf[t][8 * half + 0] = bf_lo(w.x);
       vf[t][8 * half + 1] = bf_hi(w.x);
       vf[t][8 * half + 2] = bf_lo(w.y);
@@ -133,10 +152,10 @@ __device__ __forceinline__ void compute_step(State<G>& S, const Step& st, const 
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float mn = fmaxf(S.m[h], fmaxf(s[0][h], s[1][h]));
+    const float mn = fmaxf(S.m[h], fmaxf(sc[0][h], sc[1][h]));
     const float alpha = __builtin_amdgcn_exp2f(S.m[h] - mn);
-    const float p0 = __builtin_amdgcn_exp2f(s[0][h] - mn);
-    const float p1 = __builtin_amdgcn_exp2f(s[1][h] - mn);
+    const float p0 = __builtin_amdgcn_exp2f(sc[0][h] - mn);
+    const float p1 = __builtin_amdgcn_exp2f(sc[1][h] - mn);
     S.l[h] = S.l[h] * alpha + (p0 + p1);
 #pragma unroll
     for (int d = 0; d < 16; ++d) S.o[h][d] = S.o[h][d] * alpha + p0 * vf[0][d] + p1 * vf[1][d];
@@ -144,172 +163,304 @@ __device__ __forceinline__ void compute_step(State<G>& S, const Step& st, const 
   }
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+__device__ __forceinline__ int clamp_len(int L, int max_ctx) { return L < 0 ? 0 : (L > max_ctx ? max_ctx : L); }
+
+// Work-group scan of per-sequence step counts into LDS: pre[b] = first global
+// step of sequence b, pre[S] = total.
+__device__ void scan_steps(int* pre, const int32_t* __restrict__ ctx, int S, int max_ctx, int step_tok) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x;
+  const int per = (S + 255) / 256;
+  const int lo = tid * per;
+  const int hi = lo + per < S ? lo + per : S;
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) sum += (clamp_len(ctx[b], max_ctx) + step_tok - 1) / step_tok;
+  int x = sum;  // inclusive scan inside the wavefront
+  const int lane = tid & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[tid >> 6] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
+  int run = base + x - sum;
+  for (int b = lo; b < hi; ++b) {
+    pre[b] = run;
+    run += (clamp_len(ctx[b], max_ctx) + step_tok - 1) / step_tok;
+  }
+  if (tid == 255) pre[S] = base + x;
+  __syncthreads();
+}
+
+template <int G, int HKV>
+__global__ __launch_bounds__(256) void decode_stream_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables, int bt_stride,
-    const int32_t* __restrict__ context_lens, int hq, int hkv, int64_t num_blocks, float scale_log2,
-    int max_ctx, int split, int nsplit_max, float* __restrict__ part_o, float* __restrict__ part_ml) {
-  const int g = blockIdx.x;
-  const int j = blockIdx.y;
-  const int b = blockIdx.z;
-  int L = context_lens[b];
-  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
-  const int nsplit = (L + split - 1) / split;
-  if (j >= (nsplit > 1 ? nsplit : 1)) return;
+    const int32_t* __restrict__ context_lens, int num_seqs, int64_t num_blocks, float scale_log2, int max_ctx,
+    int32_t* __restrict__ header, float* __restrict__ part_ml, float* __restrict__ part_o) {
+  constexpr int TW = 8 / HKV;       // tokens per window (one load covers TW token rows)
+  constexpr int STEP_TOK = 2 * TW;  // tokens per step
+  constexpr int HQ = G * HKV;
+  extern __shared__ int pre[];      // [num_seqs + 1]
+
+  scan_steps(pre, context_lens, num_seqs, max_ctx, STEP_TOK);
+  const int T = pre[num_seqs];
+  const int W = gridDim.x * 4;
+  int P = (T + W - 1) / W;
+  P = P > kMinStepsPerWave ? P : kMinStepsPerWave;
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= num_seqs; i += 256) header[2 + i] = pre[i];
+    if (threadIdx.x == 0) {
+      header[0] = P;
+      header[1] = T;
+    }
+  }
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int s0 = w * P;
+  if (s0 >= T) return;
+  const int s1 = s0 + P < T ? s0 + P : T;
   const int grp = lane >> 3;
   const int li = lane & 7;
+  const int kvh = grp % HKV;
 
-  u32x4 qa[G], qb[G];
-  const uint16_t* qrow = q + ((int64_t)b * hq + (int64_t)g * G) * kHeadDim;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    qa[h] = *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 8 * li);
-    qb[h] = *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 64 + 8 * li);
+  // sequence holding global step s0: pre[lo] <= s0 < pre[lo + 1]
+  int lo_b = 0, hi_b = num_seqs;
+  while (hi_b - lo_b > 1) {
+    const int mid = (lo_b + hi_b) >> 1;
+    if (pre[mid] <= s0) lo_b = mid; else hi_b = mid;
   }
+  const int b0 = __builtin_amdgcn_readfirstlane(lo_b);
 
+  auto next_seq = [&](int b) -> int {  // next sequence with at least one step (num_seqs if none)
+    int nb = b + 1;
+    while (nb < num_seqs && pre[nb + 1] == pre[nb]) ++nb;
+    return nb;
+  };
+  auto bt_row = [&](int b, uint32_t& r0, uint32_t& r1) {  // lane i: entries i and 64 + i
+    const int32_t* row = block_tables + (int64_t)(b < num_seqs ? b : 0) * bt_stride;
+    r0 = lane < bt_stride ? (uint32_t)row[lane] : 0u;
+    r1 = 64 + lane < bt_stride ? (uint32_t)row[64 + lane] : 0u;
+  };
+  auto q_row = [&](int b, auto& xa, auto& xb) {
+    const uint16_t* qp = q + ((int64_t)(b < num_seqs ? b : 0) * HQ + kvh * G) * kHeadDim + 8 * li;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      xa[h] = *reinterpret_cast<const u32x4*>(qp + h * kHeadDim);
+      xb[h] = *reinterpret_cast<const u32x4*>(qp + h * kHeadDim + 64);
+    }
+  };
+
+  // ---- load position: sequence, step, block-table rows (current and next) ----
+  int ld_b = b0;
+  int ld_s = s0 - pre[b0];
+  int ld_L = clamp_len(context_lens[ld_b], max_ctx);
+  int ld_n = pre[ld_b + 1] - pre[ld_b];
+  uint32_t bt0, bt1, btn0, btn1;
+  bt_row(ld_b, bt0, bt1);
+  int ld_next = next_seq(ld_b);
+  bt_row(ld_next, btn0, btn1);
+  int ld_next_L = ld_next < num_seqs ? clamp_len(context_lens[ld_next], max_ctx) : 0;
+  int ld_g = s0;  // global index of the load position
+
+  auto make_step = [&]() -> Step {
+    Step st;
+    const int tok0 = ld_s * STEP_TOK;
+    const int j = tok0 >> 8;
+    int64_t blk;
+    if (j < 64) blk = (int32_t)__builtin_amdgcn_readlane(bt0, j);
+    else if (j < 128) blk = (int32_t)__builtin_amdgcn_readlane(bt1, j - 64);
+    else blk = block_tables[(int64_t)ld_b * bt_stride + j];
+    if (blk < 0 || blk >= num_blocks) blk = 0;  // caller error: stay inside the pool
+    st.b = ld_b;
+    st.s = ld_s;
+    st.row0 = blk * kBlockSize + (tok0 & (kBlockSize - 1));
+    st.last_valid_row_off = ld_L - 1 - tok0;
+    st.live = true;
+    return st;
+  };
+  auto advance_load = [&]() {
+    ++ld_g;
+    if (++ld_s == ld_n && ld_g < s1) {
+      ld_b = ld_next;
+      ld_s = 0;
+      ld_L = ld_next_L;
+      ld_n = pre[ld_b + 1] - pre[ld_b];
+      bt0 = btn0;
+      bt1 = btn1;
+      ld_next = next_seq(ld_b);
+      bt_row(ld_next, btn0, btn1);
+      ld_next_L = ld_next < num_seqs ? clamp_len(context_lens[ld_next], max_ctx) : 0;
+    }
+  };
+  auto padding_step = [](const Step& like) {
+    Step st = like;
+    st.live = false;
+    return st;
+  };
+
+  // ---- compute position: queries of its sequence (and, for G <= 2, of the
+  // next one, prefetched; larger groups reload at the switch to save registers)
+  constexpr bool kPrefetchQ = G <= 2;
+  constexpr int GN = kPrefetchQ ? G : 1;
+  u32x4 qa[G], qb[G], qna[GN], qnb[GN];
+  q_row(b0, qa, qb);
+  if constexpr (kPrefetchQ) q_row(next_seq(b0), qna, qnb);
   State<G> S;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    S.m[h] = kNegBig;
-    S.l[h] = 0.f;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) S.o[h][d] = 0.f;
-  }
-
-  if (L > 0) {
-    const int t0 = j * split;
-    const int t1 = t0 + split < L ? t0 + split : L;
-    const int nstep = (t1 - t0 + 63) >> 6;  // 64 tokens per work-group step
-    const int32_t* bt = block_tables + (int64_t)b * bt_stride;
-    // a block id outside the pool is a caller error: read block 0 instead
-    // (stays inside the cache; the result is unspecified)
-    auto block_of = [&](int base) -> int64_t {
-      const int64_t blk = bt[base >> 8];
-      return (blk >= 0 && blk < num_blocks) ? blk : 0;
-    };
-    Step A, B;
-    load_step(A, k_cache, v_cache, block_of(t0), t0, wave, grp, li, t1, hkv, g);
+  auto reset = [&]() {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      retire(qa[h]);
-      retire(qb[h]);
+      S.m[h] = kNegBig;
+      S.l[h] = 0.f;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) S.o[h][d] = 0.f;
     }
-    // Loads of the next step are issued unconditionally (the last one
-    // re-reads the final step, an L2 hit) so that no wait is merged across
-    // a conditional load.
-    const int last = t0 + (nstep - 1) * 64;
-    for (int it = 0; it < nstep; it += 2) {
-      const int baseA = t0 + it * 64;
-      const int baseB = baseA + 64 < last ? baseA + 64 : last;
-      const int baseN = baseA + 128 < last ? baseA + 128 : last;
-      load_step(B, k_cache, v_cache, block_of(baseB), baseB, wave, grp, li, t1, hkv, g);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-      compute_step<G>(S, A, qa, qb, baseA, wave, grp, t1, scale_log2);
-      load_step(A, k_cache, v_cache, block_of(baseN), baseN, wave, grp, li, t1, hkv, g);
-      __builtin_amdgcn_sched_barrier(0);
-      // unconditional so that B's loads stay ahead of compute(A); a step past
-      // the split end (odd step counts only) is fully masked
-      compute_step<G>(S, B, qa, qb, baseA + 64, wave, grp, it + 1 < nstep ? t1 : 0, scale_log2);
-    }
-  }
+  };
+  reset();
+  int piece_first = s0;  // global index of the current piece's first step
 
-  // ---- combine the 8 lane groups of this wavefront ----
+  // After the last step of a piece (sequence end or range end): combine the
+  // lane groups of each head, then write the output or a partial.
+  auto finish_piece = [&](const Step& st, int gidx) {
+    const int pb = pre[st.b];
+    const int nb = pre[st.b + 1] - pb;
+    if (HKV < 8) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int off = 8 * HKV; off < 64; off <<= 1) {
+          const float mo = __shfl_xor(S.m[h], off);
+          const float mn = fmaxf(S.m[h], mo);
+          const float fa = __builtin_amdgcn_exp2f(S.m[h] - mn);
+          const float fb = __builtin_amdgcn_exp2f(mo - mn);
+          S.l[h] = S.l[h] * fa + __shfl_xor(S.l[h], off) * fb;
+#pragma unroll
+          for (int d = 0; d < 16; ++d) S.o[h][d] = S.o[h][d] * fa + __shfl_xor(S.o[h][d], off) * fb;
+          S.m[h] = mn;
+        }
+      }
+    }
+    const bool whole = (pb / P) == ((pb + nb - 1) / P);
+    if (grp < HKV) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int head = kvh * G + h;
+        if (whole) {
+          const float inv = 1.f / S.l[h];
+          u32x4 a, c;
+          a.x = pack_bf16x2(S.o[h][0] * inv, S.o[h][1] * inv);
+          a.y = pack_bf16x2(S.o[h][2] * inv, S.o[h][3] * inv);
+          a.z = pack_bf16x2(S.o[h][4] * inv, S.o[h][5] * inv);
+          a.w = pack_bf16x2(S.o[h][6] * inv, S.o[h][7] * inv);
+          c.x = pack_bf16x2(S.o[h][8] * inv, S.o[h][9] * inv);
+          c.y = pack_bf16x2(S.o[h][10] * inv, S.o[h][11] * inv);
+          c.z = pack_bf16x2(S.o[h][12] * inv, S.o[h][13] * inv);
+          c.w = pack_bf16x2(S.o[h][14] * inv, S.o[h][15] * inv);
+          uint16_t* op = out + ((int64_t)st.b * HQ + head) * kHeadDim + 8 * li;
+          *reinterpret_cast<u32x4*>(op) = a;
+          *reinterpret_cast<u32x4*>(op + 64) = c;
+        } else {
+          const int slot = (piece_first == s0) ? 0 : 1;
+          const int64_t pidx = ((int64_t)w * 2 + slot) * HQ + head;
+          float* po = part_o + pidx * kHeadDim + 8 * li;
+          *reinterpret_cast<f32x4*>(po) = f32x4{S.o[h][0], S.o[h][1], S.o[h][2], S.o[h][3]};
+          *reinterpret_cast<f32x4*>(po + 4) = f32x4{S.o[h][4], S.o[h][5], S.o[h][6], S.o[h][7]};
+          *reinterpret_cast<f32x4*>(po + 64) = f32x4{S.o[h][8], S.o[h][9], S.o[h][10], S.o[h][11]};
+          *reinterpret_cast<f32x4*>(po + 68) = f32x4{S.o[h][12], S.o[h][13], S.o[h][14], S.o[h][15]};
+          if (li == 0) {
+            part_ml[pidx * 2 + 0] = S.m[h];
+            part_ml[pidx * 2 + 1] = S.l[h];
+          }
+        }
+      }
+    }
+    reset();
+    piece_first = gidx + 1;
+    if (st.s + 1 == nb) {  // the sequence ended: move to the next one's queries
+      if constexpr (kPrefetchQ) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          qa[h] = qna[h];
+          qb[h] = qnb[h];
+        }
+        q_row(next_seq(next_seq(st.b)), qna, qnb);
+      } else {
+        q_row(next_seq(st.b), qa, qb);
+      }
+    }
+  };
+  auto ends_piece = [&](const Step& st, int gidx) {
+    return st.s + 1 == pre[st.b + 1] - pre[st.b] || gidx + 1 == s1;
+  };
+
+  Buf A, B;
+  Step sa = make_step();
+  load_buf<HKV>(A, k_cache, v_cache, sa, grp, li);
+  advance_load();
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float mw = fmaxf(S.m[h], dpp<kRowRor8>(S.m[h]));
-    mw = fmaxf(mw, __shfl_xor(mw, 16));
-    mw = fmaxf(mw, __shfl_xor(mw, 32));
-    const float f = __builtin_amdgcn_exp2f(S.m[h] - mw);
-    float lw = S.l[h] * f;
-    lw += dpp<kRowRor8>(lw);
-    lw += __shfl_xor(lw, 16);
-    lw += __shfl_xor(lw, 32);
-    S.l[h] = lw;
-    S.m[h] = mw;
-#pragma unroll
-    for (int d = 0; d < 16; ++d) {
-      float x = S.o[h][d] * f;
-      x += dpp<kRowRor8>(x);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      S.o[h][d] = x;
-    }
+    retire(qa[h]);
+    retire(qb[h]);
   }
-
-  // ---- combine the 4 wavefronts through LDS ----
-  __shared__ float lds_o[4][G][kHeadDim];
-  __shared__ float lds_m[4][G];
-  __shared__ float lds_l[4][G];
-  if (grp == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        lds_o[wave][h][8 * li + d] = S.o[h][d];
-        lds_o[wave][h][64 + 8 * li + d] = S.o[h][8 + d];
-      }
-      if (li == 0) {
-        lds_m[wave][h] = S.m[h];
-        lds_l[wave][h] = S.l[h];
-      }
-    }
-  }
-  __syncthreads();
-  for (int t = threadIdx.x; t < G * kHeadDim; t += 256) {
-    const int h = t / kHeadDim;
-    const int d = t % kHeadDim;
-    float M = lds_m[0][h];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, lds_m[w][h]);
-    float o = 0.f, l = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = __builtin_amdgcn_exp2f(lds_m[w][h] - M);
-      o += lds_o[w][h][d] * f;
-      l += lds_l[w][h] * f;
-    }
-    const int64_t qh = (int64_t)b * hq + (int64_t)g * G + h;
-    if (nsplit <= 1) {
-      const float r = L > 0 ? o / l : 0.f;
-      out[qh * kHeadDim + d] = (uint16_t)f32_to_bf16_bits(r);
-    } else {
-      const int64_t pidx = qh * nsplit_max + j;
-      part_o[pidx * kHeadDim + d] = o;
-      if (d == 0) {
-        part_ml[pidx * 2 + 0] = M;
-        part_ml[pidx * 2 + 1] = l;
-      }
-    }
+  for (int gi = s0; gi < s1; gi += 2) {
+    // The loads of the following step are issued unconditionally (a padding
+    // step past the range re-reads rows just fetched and is fully masked),
+    // so they are never sunk below the compute of the current step.
+    const bool hasB = gi + 1 < s1;
+    const Step sb = hasB ? make_step() : padding_step(sa);
+    load_buf<HKV>(B, k_cache, v_cache, sb, grp, li);
+    if (hasB) advance_load();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_buf<G, HKV>(S, A, qa, qb, sa, grp, scale_log2);
+    if (ends_piece(sa, gi)) finish_piece(sa, gi);
+    const bool hasA = gi + 2 < s1;
+    const Step sn = hasA ? make_step() : padding_step(sb);
+    load_buf<HKV>(A, k_cache, v_cache, sn, grp, li);
+    if (hasA) advance_load();
+    __builtin_amdgcn_sched_barrier(0);
+    compute_buf<G, HKV>(S, B, qa, qb, sb, grp, scale_log2);
+    if (hasB && ends_piece(sb, gi + 1)) finish_piece(sb, gi + 1);
+    sa = sn;
   }
 }
 
-// One wavefront per (seq, q head): combine the splits' (m, l, o).
+// One wavefront per (seq, q head): combine the pieces of a sequence that was
+// split between wavefronts; zeros for padding rows (context 0).
 __global__ __launch_bounds__(64) void decode_merge_kernel(uint16_t* __restrict__ out,
-                                                          const float* __restrict__ part_o,
+                                                          const int32_t* __restrict__ header,
                                                           const float* __restrict__ part_ml,
-                                                          const int32_t* __restrict__ context_lens, int hq,
-                                                          int max_ctx, int split, int nsplit_max) {
+                                                          const float* __restrict__ part_o,
+                                                          const int32_t* __restrict__ context_lens, int hq) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
-  int L = context_lens[b];
-  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
-  const int ns = (L + split - 1) / split;
-  if (ns <= 1) return;
   const int lane = threadIdx.x;
   const int64_t qh = (int64_t)b * hq + h;
-  const float* ml = part_ml + qh * nsplit_max * 2;
+  if (context_lens[b] <= 0) {
+    reinterpret_cast<uint32_t*>(out + qh * kHeadDim)[lane] = 0u;
+    return;
+  }
+  const int P = header[0];
+  const int pb = header[2 + b];
+  const int nb = header[3 + b] - pb;
+  const int wf = pb / P;
+  const int wl = (pb + nb - 1) / P;
+  if (wf == wl) return;  // written whole by its wavefront
   float M = kNegBig;
-  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[2 * j]);
+  for (int w = wf; w <= wl; ++w) {
+    const int slot = (w == wf && pb != w * P) ? 1 : 0;
+    M = fmaxf(M, part_ml[(((int64_t)w * 2 + slot) * hq + h) * 2]);
+  }
   float a0 = 0.f, a1 = 0.f, lsum = 0.f;
-  const float* po = part_o + qh * nsplit_max * kHeadDim + 2 * lane;
-  for (int j = 0; j < ns; ++j) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * j] - M);
-    lsum += ml[2 * j + 1] * f;
-    const float2 o = *reinterpret_cast<const float2*>(po + (int64_t)j * kHeadDim);
+  for (int w = wf; w <= wl; ++w) {
+    const int slot = (w == wf && pb != w * P) ? 1 : 0;
+    const int64_t pidx = ((int64_t)w * 2 + slot) * hq + h;
+    const float f = __builtin_amdgcn_exp2f(part_ml[pidx * 2] - M);
+    lsum += part_ml[pidx * 2 + 1] * f;
+    const float2 o = *reinterpret_cast<const float2*>(part_o + pidx * kHeadDim + 2 * lane);
     a0 += o.x * f;
     a1 += o.y * f;
   }
@@ -317,27 +468,66 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(uint16_t* __restrict__
   reinterpret_cast<uint32_t*>(out + qh * kHeadDim)[lane] = pack_bf16x2(a0 * inv, a1 * inv);
 }
 
-}  // namespace
+struct Layout {
+  size_t header_bytes, ml_bytes, o_bytes;
+};
 
-// Tokens per split: a multiple of 64 (so a 64-token step never straddles a
-// 256-token block). Longer splits for larger query groups keep the partials
-// small against the K/V bytes; shorter ones when there are too few
-// work-groups to fill the chip.
-static int decode_split_tokens(int num_seqs, int hq, int hkv, int max_ctx) {
-  const int G = hq / hkv;
-  int split = G >= 4 ? 512 : 256;
-  while (split > 64) {
-    const int64_t wgs = (int64_t)num_seqs * hkv * ((max_ctx + split - 1) / split);
-    if (wgs >= 2048) break;
-    split /= 2;
+Layout workspace_layout(int num_seqs, int num_q_heads) {
+  Layout lo;
+  lo.header_bytes = ((size_t)(num_seqs + 3) * 4 + 255) & ~(size_t)255;
+  lo.ml_bytes = ((size_t)kWavesCap * 2 * num_q_heads * 2 * 4 + 255) & ~(size_t)255;
+  lo.o_bytes = (size_t)kWavesCap * 2 * num_q_heads * kHeadDim * 4;
+  return lo;
+}
+
+template <int G, int HKV>
+const void* stream_kernel() {
+  return reinterpret_cast<const void*>(&decode_stream_kernel<G, HKV>);
+}
+
+const void* pick_kernel(int G, int hkv) {
+#define PKV_PICK(GG)                       \
+  switch (hkv) {                           \
+    case 1: return stream_kernel<GG, 1>(); \
+    case 2: return stream_kernel<GG, 2>(); \
+    case 4: return stream_kernel<GG, 4>(); \
+    default: return stream_kernel<GG, 8>(); \
   }
-  return split;
+  switch (G) {
+    case 1: PKV_PICK(1)
+    case 2: PKV_PICK(2)
+    case 4: PKV_PICK(4)
+    default: PKV_PICK(8)
+  }
+#undef PKV_PICK
 }
 
-static int decode_nsplit_max(int split, int max_ctx) {
-  const int n = (max_ctx + split - 1) / split;
-  return n > 1 ? n : 1;
+// Resident work-groups of a decode kernel on the current device (cached per
+// device, kernel and LDS size), capped so the partial slots suffice; 0 on error.
+int resident_wgs(const void* kernel, size_t lds) {
+  static std::mutex mu;
+  static struct Entry {
+    int dev;
+    const void* k;
+    size_t lds;
+    int n;
+  } cache[128];
+  static int ncache = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < ncache; ++i)
+    if (cache[i].dev == dev && cache[i].k == kernel && cache[i].lds == lds) return cache[i].n;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, lds) != hipSuccess || per < 1) per = 1;
+  int n = cus * per;
+  if (n * 4 > kWavesCap) n = kWavesCap / 4;
+  if (ncache < 128) cache[ncache++] = Entry{dev, kernel, lds, n};
+  return n;
 }
+
+}  // namespace
 
 }  // namespace pkv
 
@@ -347,13 +537,8 @@ extern "C" size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim != kHeadDim || max_context_len < 0 ||
       num_q_heads % num_kv_heads)
     return 0;
-  const int split = decode_split_tokens(num_seqs, num_q_heads, num_kv_heads, max_context_len);
-  const int64_t ns = decode_nsplit_max(split, max_context_len);
-  const int64_t units = (int64_t)num_seqs * num_q_heads * ns;
-  size_t bytes = (size_t)units * kHeadDim * 4;
-  bytes = (bytes + 255) & ~(size_t)255;
-  bytes += (size_t)units * 2 * 4;
-  return (bytes + 255) & ~(size_t)255;
+  const Layout lo = workspace_layout(num_seqs, num_q_heads);
+  return lo.header_bytes + lo.ml_bytes + lo.o_bytes;
 }
 
 extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -368,7 +553,9 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
   if (head_dim != kHeadDim) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: head_dim %d (128 only)", head_dim);
   if (block_size != kBlockSize)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: block_size %d (256 only)", block_size);
-  if (num_kv_heads < 1 || num_kv_heads > 64 || num_q_heads < 1 || num_q_heads % num_kv_heads)
+  if (num_kv_heads != 1 && num_kv_heads != 2 && num_kv_heads != 4 && num_kv_heads != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: num_kv_heads %d (1, 2, 4 or 8)", num_kv_heads);
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: head counts %d/%d unsupported", num_q_heads, num_kv_heads);
   const int G = num_q_heads / num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8)
@@ -376,6 +563,7 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
   if (!(scale > 0.f) || !__builtin_isfinite(scale))
     return fail(PKV_ERR_INVALID, "paged_attn_decode: scale must be finite and > 0");
   if (num_seqs == 0) return ok();
+  if (num_seqs > kMaxSeqs) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: more than %d sequences", kMaxSeqs);
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID, "paged_attn_decode: null pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -384,45 +572,48 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
   if (block_table_stride < need_bt)
     return fail(PKV_ERR_INVALID, "paged_attn_decode: block_table_stride %d < %lld blocks of max_context_len",
                 block_table_stride, (long long)need_bt);
-  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: more than 65535 sequences");
-  const int split = decode_split_tokens(num_seqs, num_q_heads, num_kv_heads, max_context_len);
-  const int nsplit_max = decode_nsplit_max(split, max_context_len);
   const size_t ws = paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len);
-  if (nsplit_max > 1 && (!workspace || workspace_bytes < ws))
+  if (!workspace || workspace_bytes < ws)
     return fail(PKV_ERR_WORKSPACE, "paged_attn_decode: workspace of %zu bytes needed, got %zu", ws, workspace_bytes);
-  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255))
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: workspace must be 256-byte aligned");
-  if (nsplit_max > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: context too long");
 
-  const int64_t units = (int64_t)num_seqs * num_q_heads * nsplit_max;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_ml = workspace ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                        ((units * kHeadDim * 4 + 255) & ~(int64_t)255))
-                             : nullptr;
+  const Layout lo = workspace_layout(num_seqs, num_q_heads);
+  char* wsb = static_cast<char*>(workspace);
+  int32_t* header = reinterpret_cast<int32_t*>(wsb);
+  float* part_ml = reinterpret_cast<float*>(wsb + lo.header_bytes);
+  float* part_o = reinterpret_cast<float*>(wsb + lo.header_bytes + lo.ml_bytes);
   const float scale_log2 = scale * 1.4426950408889634f;
+  const size_t lds = (size_t)(num_seqs + 1) * 4;
+  const int grid = resident_wgs(pick_kernel(G, num_kv_heads), lds);
+  if (grid <= 0) return fail(PKV_ERR_HIP, "paged_attn_decode: cannot query the device");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  dim3 grid(num_kv_heads, nsplit_max, num_seqs);
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const char* kc = static_cast<const char*>(k_cache);
   const char* vc = static_cast<const char*>(v_cache);
-#define PKV_DECODE_LAUNCH(GG)                                                                                   \
-  hipLaunchKernelGGL(decode_split_kernel<GG>, grid, dim3(256), 0, s, o, qq, kc, vc, block_tables,               \
-                     block_table_stride, context_lens, num_q_heads, num_kv_heads, num_blocks, scale_log2,      \
-                     max_context_len, split, nsplit_max, part_o, part_ml)
+#define PKV_DECODE_LAUNCH(GG, HH)                                                                         \
+  hipLaunchKernelGGL((decode_stream_kernel<GG, HH>), dim3(grid), dim3(256), lds, s, o, qq, kc, vc,       \
+                     block_tables, block_table_stride, context_lens, num_seqs, num_blocks, scale_log2,   \
+                     max_context_len, header, part_ml, part_o)
+#define PKV_DECODE_HKV(GG)                    \
+  switch (num_kv_heads) {                     \
+    case 1: PKV_DECODE_LAUNCH(GG, 1); break;  \
+    case 2: PKV_DECODE_LAUNCH(GG, 2); break;  \
+    case 4: PKV_DECODE_LAUNCH(GG, 4); break;  \
+    default: PKV_DECODE_LAUNCH(GG, 8); break; \
+  }
   switch (G) {
-    case 1: PKV_DECODE_LAUNCH(1); break;
-    case 2: PKV_DECODE_LAUNCH(2); break;
-    case 4: PKV_DECODE_LAUNCH(4); break;
-    default: PKV_DECODE_LAUNCH(8); break;
+    case 1: PKV_DECODE_HKV(1) break;
+    case 2: PKV_DECODE_HKV(2) break;
+    case 4: PKV_DECODE_HKV(4) break;
+    default: PKV_DECODE_HKV(8) break;
   }
+#undef PKV_DECODE_HKV
 #undef PKV_DECODE_LAUNCH
-  pkv_status st = check_launch("paged_attn_decode (split)");
+  pkv_status st = check_launch("paged_attn_decode (stream)");
   if (st != PKV_OK) return st;
-  if (nsplit_max > 1) {
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, num_seqs), dim3(64), 0, s, o, part_o, part_ml,
-                       context_lens, num_q_heads, max_context_len, split, nsplit_max);
-    return check_launch("paged_attn_decode (merge)");
-  }
-  return ok();
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, num_seqs), dim3(64), 0, s, o, header, part_ml, part_o,
+                     context_lens, num_q_heads);
+  return check_launch("paged_attn_decode (merge)");
 }
