@@ -129,9 +129,12 @@ pkv_status kv_store(const void* key, int64_t key_token_stride, const void* value
  * store runs first, so the context includes the current token).
  *
  * paged_attn_decode_workspace_size returns the bytes of device workspace
- * paged_attn_decode needs for these sizes (fp32 partial results of the
- * split-K pass). It depends only on its arguments; 0 is never returned for a
- * non-empty problem.
+ * paged_attn_decode needs: a small header (work split) followed by fp32
+ * partial results of sequences split between wavefronts (a fixed number of
+ * slots per wavefront of the persistent grid). It depends only on its
+ * arguments; 0 means unsupported arguments. Its contents need no
+ * initialisation; calls that overlap on different streams need different
+ * workspaces.
  */
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
@@ -156,9 +159,11 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *   workspace        device memory of at least workspace_size bytes (256-byte
  *                    aligned), owned by the caller, reusable across calls on
  *                    one stream
- * Supported: head_dim 128, block_size 256, num_q_heads / num_kv_heads in
- * {1, 2, 4, 8}, num_kv_heads <= 64.
- * Results are deterministic (a fixed split plan; no atomics).
+ * Supported: head_dim 128, block_size 256, num_kv_heads in {1, 2, 4, 8},
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}, num_seqs <= 8192.
+ * Results are deterministic: the split of the work depends only on the
+ * context lengths and the device's resident wavefront count, and partial
+ * results are combined in a fixed order (no atomics).
  */
 pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, int32_t block_table_stride,

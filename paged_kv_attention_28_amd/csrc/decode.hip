@@ -1,6 +1,6 @@
 // paged_attn_decode: one query token per sequence, context read through the
-// block table; a persistent stream-K pass over all context rows plus a merge
-// of the sequences that were split between wavefronts.
+// block table; a persistent stream-K kernel over all context rows, then one
+// wavefront per sequence merges the sequences split between wavefronts.
 //
 // P1 = "13. 读一个最小推理引擎：nano-vllm", section "第六站：注意力层": decode
 // attends its whole history, read from the paged cache through the block
@@ -28,9 +28,12 @@
 //  * A wavefront that owns a whole sequence writes the normalised bf16
 //    output. A sequence cut between wavefronts leaves one fp32 (m, l, o)
 //    partial per piece, in slot 0 (piece starts the wavefront's range) or
-//    slot 1 (piece ends it) of that wavefront; the merge kernel finds the
-//    pieces from the same step arithmetic and combines them (log-sum-exp in
-//    the log2 domain), and writes zeros for padding rows (context 0).
+//    slot 1 (piece ends it) of that wavefront. The merge kernel (one
+//    work-group per sequence, all heads at once) finds the pieces from the
+//    same step arithmetic and combines them (log-sum-exp in the log2
+//    domain); it also writes zeros for padding rows (context 0). (Merging
+//    inside the stream kernel would need a device-scope release per piece,
+//    which writes back the whole L2 of the XCD on this GPU.)
 //  * Positions past the context end load the last context row (always
 //    written) and get a score of -inf: stale or poisoned cache rows never
 //    enter the result.
@@ -195,6 +198,72 @@ __device__ void scan_steps(int* pre, const int32_t* __restrict__ ctx, int S, int
   __syncthreads();
 }
 
+// One work-group per sequence, 16 lanes per query head (8 dims per lane):
+// zeros for a padding row (context 0); for a sequence split between
+// wavefronts, an online log-sum-exp combination of its pieces (partials of
+// up to 4 pieces are loaded at once); nothing for a sequence written whole.
+// Pieces are the wavefronts wf .. wf + npieces - 1; the first one's partial
+// is in slot 1 unless the sequence starts exactly at that wavefront's range.
+template <int HQ>
+__global__ __launch_bounds__(HQ * 16) void decode_merge_kernel(uint16_t* __restrict__ out,
+                                                               const int32_t* __restrict__ header,
+                                                               const float* __restrict__ part_ml,
+                                                               const float* __restrict__ part_o,
+                                                               const int32_t* __restrict__ context_lens) {
+  const int b = blockIdx.x;
+  const int h = threadIdx.x >> 4;
+  const int d0 = 8 * (threadIdx.x & 15);
+  const int L = context_lens[b];
+  const int P = header[0];
+  const int pb = header[1 + b];
+  const int nb = header[2 + b] - pb;
+  u32x4* op = reinterpret_cast<u32x4*>(out + ((int64_t)b * HQ + h) * kHeadDim + d0);
+  if (L <= 0 || nb <= 0) {
+    *op = u32x4{0, 0, 0, 0};
+    return;
+  }
+  const int wf = pb / P;
+  const int npieces = (pb + nb - 1) / P - wf + 1;
+  if (npieces == 1) return;
+  float M = kNegBig, lsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < npieces; i0 += 4) {
+    float m[4], l[4];
+    f32x4 lo[4], hi[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = i0 + k < npieces ? i0 + k : npieces - 1;
+      const int w = wf + i;
+      const int slot = (i == 0 && pb != w * P) ? 1 : 0;
+      const int64_t pidx = ((int64_t)w * 2 + slot) * HQ + h;
+      m[k] = part_ml[pidx * 2];
+      l[k] = part_ml[pidx * 2 + 1];
+      lo[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0);
+      hi[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0 + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (i0 + k >= npieces) break;
+      const float mn = fmaxf(M, m[k]);
+      const float fa = __builtin_amdgcn_exp2f(M - mn);
+      const float fb = __builtin_amdgcn_exp2f(m[k] - mn);
+      lsum = lsum * fa + l[k] * fb;
+      acc[0] = acc[0] * fa + lo[k].x * fb;
+      acc[1] = acc[1] * fa + lo[k].y * fb;
+      acc[2] = acc[2] * fa + lo[k].z * fb;
+      acc[3] = acc[3] * fa + lo[k].w * fb;
+      acc[4] = acc[4] * fa + hi[k].x * fb;
+      acc[5] = acc[5] * fa + hi[k].y * fb;
+      acc[6] = acc[6] * fa + hi[k].z * fb;
+      acc[7] = acc[7] * fa + hi[k].w * fb;
+      M = mn;
+    }
+  }
+  const float inv = 1.f / lsum;
+  *op = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+              pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+}
+
 template <int G, int HKV>
 __global__ __launch_bounds__(256) void decode_stream_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
@@ -211,12 +280,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   const int W = gridDim.x * 4;
   int P = (T + W - 1) / W;
   P = P > kMinStepsPerWave ? P : kMinStepsPerWave;
-  if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i <= num_seqs; i += 256) header[2 + i] = pre[i];
-    if (threadIdx.x == 0) {
-      header[0] = P;
-      header[1] = T;
-    }
+  if (blockIdx.x == 0) {  // step prefix for the merge kernel
+    for (int i = threadIdx.x; i <= num_seqs; i += 256) header[1 + i] = pre[i];
+    if (threadIdx.x == 0) header[0] = P;
   }
 
   const int lane = threadIdx.x & 63;
@@ -428,53 +494,13 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   }
 }
 
-// One wavefront per (seq, q head): combine the pieces of a sequence that was
-// split between wavefronts; zeros for padding rows (context 0).
-__global__ __launch_bounds__(64) void decode_merge_kernel(uint16_t* __restrict__ out,
-                                                          const int32_t* __restrict__ header,
-                                                          const float* __restrict__ part_ml,
-                                                          const float* __restrict__ part_o,
-                                                          const int32_t* __restrict__ context_lens, int hq) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int64_t qh = (int64_t)b * hq + h;
-  if (context_lens[b] <= 0) {
-    reinterpret_cast<uint32_t*>(out + qh * kHeadDim)[lane] = 0u;
-    return;
-  }
-  const int P = header[0];
-  const int pb = header[2 + b];
-  const int nb = header[3 + b] - pb;
-  const int wf = pb / P;
-  const int wl = (pb + nb - 1) / P;
-  if (wf == wl) return;  // written whole by its wavefront
-  float M = kNegBig;
-  for (int w = wf; w <= wl; ++w) {
-    const int slot = (w == wf && pb != w * P) ? 1 : 0;
-    M = fmaxf(M, part_ml[(((int64_t)w * 2 + slot) * hq + h) * 2]);
-  }
-  float a0 = 0.f, a1 = 0.f, lsum = 0.f;
-  for (int w = wf; w <= wl; ++w) {
-    const int slot = (w == wf && pb != w * P) ? 1 : 0;
-    const int64_t pidx = ((int64_t)w * 2 + slot) * hq + h;
-    const float f = __builtin_amdgcn_exp2f(part_ml[pidx * 2] - M);
-    lsum += part_ml[pidx * 2 + 1] * f;
-    const float2 o = *reinterpret_cast<const float2*>(part_o + pidx * kHeadDim + 2 * lane);
-    a0 += o.x * f;
-    a1 += o.y * f;
-  }
-  const float inv = 1.f / lsum;
-  reinterpret_cast<uint32_t*>(out + qh * kHeadDim)[lane] = pack_bf16x2(a0 * inv, a1 * inv);
-}
-
 struct Layout {
-  size_t header_bytes, ml_bytes, o_bytes;
+  size_t header_bytes, ml_bytes, o_bytes;  // header = steps per wavefront + step prefix
 };
 
 Layout workspace_layout(int num_seqs, int num_q_heads) {
   Layout lo;
-  lo.header_bytes = ((size_t)(num_seqs + 3) * 4 + 255) & ~(size_t)255;
+  lo.header_bytes = ((size_t)(num_seqs + 2) * 4 + 255) & ~(size_t)255;
   lo.ml_bytes = ((size_t)kWavesCap * 2 * num_q_heads * 2 * 4 + 255) & ~(size_t)255;
   lo.o_bytes = (size_t)kWavesCap * 2 * num_q_heads * kHeadDim * 4;
   return lo;
@@ -613,7 +639,15 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
 #undef PKV_DECODE_LAUNCH
   pkv_status st = check_launch("paged_attn_decode (stream)");
   if (st != PKV_OK) return st;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_q_heads, num_seqs), dim3(64), 0, s, o, header, part_ml, part_o,
-                     context_lens, num_q_heads);
+  switch (num_q_heads) {  // HQ = G * H_kv, both powers of two up to 8
+#define PKV_MERGE(HQV)                                                                                          \
+  case HQV:                                                                                                     \
+    hipLaunchKernelGGL(decode_merge_kernel<HQV>, dim3(num_seqs), dim3(HQV * 16), 0, s, o, header, part_ml,      \
+                       part_o, context_lens);                                                                  \
+    break;
+    PKV_MERGE(1) PKV_MERGE(2) PKV_MERGE(4) PKV_MERGE(8) PKV_MERGE(16) PKV_MERGE(32) PKV_MERGE(64)
+#undef PKV_MERGE
+    default: return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d query heads", num_q_heads);
+  }
   return check_launch("paged_attn_decode (merge)");
 }

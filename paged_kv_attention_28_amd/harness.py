@@ -119,12 +119,16 @@ class StepRunner:
         self.out = torch.empty_like(self.q)
         m0 = meta(w, p.batch)
         rows = len(p.batch.seqs) + p.batch.num_pad
+        # one int32 buffer holds slot mapping | cu_seqlens_q | context lens |
+        # block tables, so a step uploads its metadata with a single copy
         self.shapes = (m0.num_tokens, rows + 1, rows, rows * w.max_blocks_per_seq)
-        self.pinned = []
-        for _ in range(2):
-            self.pinned.append(tuple(torch.empty(n, dtype=torch.int32).pin_memory() for n in self.shapes))
+        offs = np.concatenate([[0], np.cumsum(self.shapes)]).astype(np.int64)
+        self.offs = offs
+        total = int(offs[-1])
+        self.pinned = [torch.empty(total, dtype=torch.int32).pin_memory() for _ in range(2)]
         self.events = [None, None]
-        self.dev_meta = tuple(torch.empty(n, dtype=torch.int32, device=dev) for n in self.shapes)
+        self.dev_flat = torch.empty(total, dtype=torch.int32, device=dev)
+        self.dev_meta = tuple(self.dev_flat[offs[i]:offs[i + 1]] for i in range(4))
         self.max_q_len = m0.max_q_len
         self.max_ctx = m0.max_context_len
         self.workspace = (decode_workspace(w, rows, self.max_ctx, dev) if p.kind == "decode" else None)
@@ -136,10 +140,10 @@ class StepRunner:
         self.i += 1
         if self.events[k] is not None:
             self.events[k].synchronize()
-        bufs = self.pinned[k]
-        meta(w, p.batch, out=tuple(b.numpy() for b in bufs))
-        for d, h in zip(self.dev_meta, bufs):
-            d.copy_(h, non_blocking=True)
+        flat = self.pinned[k].numpy()
+        o = self.offs
+        meta(w, p.batch, out=tuple(flat[o[i]:o[i + 1]] for i in range(4)))
+        self.dev_flat.copy_(self.pinned[k], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
         self.events[k] = ev
