@@ -9,8 +9,9 @@ Headline (``value``): the decode step of the 256-sequence decode workload
 batch padded to 272 rows) in GB/s of algorithmic HBM bytes (K/V context read
 once, q, out, block-table entries and lengths, plus 8 KiB stored per real
 token) per wall-clock step. ``roofline`` reports the decode attention call
-(split-K kernel + merge kernel) timed with HIP events on its stream against
-the 8 TB/s HBM peak. ``prefill`` reports the chunked-prefill step (16384-token
+(persistent stream-K kernel + merge kernel) timed with HIP events on its
+stream against the 8 TB/s HBM peak; ``traffic`` is the HBM bytes per call from
+the committed rocprofv3 counter summary, or null once the kernel changed. ``prefill`` reports the chunked-prefill step (16384-token
 budget) in TFLOP/s of unmasked attention flops against the 2.5 PFLOP/s bf16
 MFMA peak. ``cpu_baseline`` times the fp64 oracle on the same decode step
 on the host before the GPU is initialised.
@@ -36,10 +37,27 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+DECODE_PROFILE = os.path.join(ROOT, "profiles", "decode_stream_kernel__decode_256seq_ctx100-2048.txt")
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_attention_28_amd", "csrc", "decode.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per paged_attn_decode call from the committed rocprofv3
+    counter summary (FETCH_SIZE / WRITE_SIZE, calibrated on a copy of known
+    size), or None when the decode source changed since it was taken."""
+    import hashlib
+    try:
+        fields = dict(l.split(":", 1) for l in open(DECODE_PROFILE) if l.startswith(("traffic_bytes:", "source_sha256:")))
+        sha = hashlib.sha256(open(DECODE_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if fields.get("source_sha256", "").strip() != sha:
+        return None
+    return int(fields["traffic_bytes"])
 
 
 # ----------------------------------------------------------------------------
@@ -156,7 +174,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU; multi-GPU runs are not supported (got --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
@@ -231,8 +249,9 @@ def main():
                    "global_batch": 272, "seq_len": int(max(s.seq_len for s in wd.store.seqs)),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attn_decode (split-K + merge), HIP events, mean over timed steps",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "paged_attn_decode call (decode_stream_kernel + decode_merge_kernel), HIP events "
+                               "on its stream, mean over the timed steps",
                      "algorithmic_bytes": db["attn"], "us": round(attn_avg * 1e3, 2)},
         "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
         "prefill": prefill,
