@@ -38,6 +38,7 @@ from .paged import (  # noqa: F401
     bf16_bits_to_f64,
     prepare_step_ref,
     kv_store_ref,
+    kv_store_inplace_ref,
     gather_context_ref,
     attn_contiguous_ref,
     decode_ref,

@@ -25,6 +25,7 @@ __all__ = [
     "bf16_bits_to_f64",
     "prepare_step_ref",
     "kv_store_ref",
+    "kv_store_inplace_ref",
     "gather_context_ref",
     "attn_contiguous_ref",
     "decode_ref",
@@ -106,8 +107,8 @@ def prepare_step_ref(seq_lens, num_cached, block_tables, block_size: int,
 # a2: KV store
 # ----------------------------------------------------------------------------
 
-def kv_store_ref(k_cache, v_cache, key, value, slot_mapping):
-    """Copy token rows into the paged cache; returns new (k_cache, v_cache).
+def kv_store_inplace_ref(k_cache, v_cache, key, value, slot_mapping) -> None:
+    """Copy token rows into the paged cache arrays in place (uint16 arrays).
 
     P1, "第六站：注意力层": one program per token reads its slot, returns early
     when the slot is -1, and copies the token's whole K row and V row (all KV
@@ -116,11 +117,14 @@ def kv_store_ref(k_cache, v_cache, key, value, slot_mapping):
 
     Readings: a slot outside [0, num_blocks * block_size) other than -1 is a
     caller error (raises); two tokens may not name the same slot in one call
-    (raises), since the result would depend on write order.
+    (raises), since the result would depend on write order. Nothing is
+    written when an error is raised.
     """
-    kc = np.array(k_cache, dtype=np.uint16, copy=True)
-    vc = np.array(v_cache, dtype=np.uint16, copy=True)
-    N, B, H, D = kc.shape
+    if k_cache.dtype != np.uint16 or v_cache.dtype != np.uint16:
+        raise TypeError("caches must be uint16 bit patterns")
+    if not (k_cache.flags.c_contiguous and v_cache.flags.c_contiguous):
+        raise ValueError("caches must be C-contiguous to be written in place")
+    N, B, H, D = k_cache.shape
     slots = np.asarray(slot_mapping, dtype=np.int64)
     key = np.asarray(key, dtype=np.uint16).reshape(len(slots), H, D)
     value = np.asarray(value, dtype=np.uint16).reshape(len(slots), H, D)
@@ -131,10 +135,15 @@ def kv_store_ref(k_cache, v_cache, key, value, slot_mapping):
             raise ValueError("slot out of range")
         if np.unique(s).size != s.size:
             raise ValueError("duplicate slot in one store")
-    kflat = kc.reshape(N * B, H, D)
-    vflat = vc.reshape(N * B, H, D)
-    kflat[s] = key[live]
-    vflat[s] = value[live]
+    k_cache.reshape(N * B, H, D)[s] = key[live]
+    v_cache.reshape(N * B, H, D)[s] = value[live]
+
+
+def kv_store_ref(k_cache, v_cache, key, value, slot_mapping):
+    """The store on copies of the caches; returns the new (k_cache, v_cache)."""
+    kc = np.array(k_cache, dtype=np.uint16, copy=True)
+    vc = np.array(v_cache, dtype=np.uint16, copy=True)
+    kv_store_inplace_ref(kc, vc, key, value, slot_mapping)
     return kc, vc
 
 

@@ -170,3 +170,55 @@ class StepRunner:
     def step(self):
         self.prepare_and_upload()
         self.kernels()
+
+
+class TraceRunner:
+    """Replays a scheduler trace (configuration 5) over several layers: each
+    step prepares its metadata on the host once, then for every layer draws
+    fresh seeded q/k/v, stores the step's K/V into that layer's caches and
+    runs prefill or decode attention."""
+
+    def __init__(self, seed: int, num_layers: int, num_blocks: int, max_blocks_per_seq: int = 8,
+                 num_q_heads: int = 16, num_kv_heads: int = 8, head_dim: int = 128, device="cuda"):
+        self.seed, self.L, self.device = seed, num_layers, device
+        self.hq, self.hkv, self.d, self.mb = num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq
+        self.shape_w = W.Workload("trace", seed, num_q_heads, num_kv_heads, head_dim, W.BLOCK_SIZE, num_blocks,
+                                  max_blocks_per_seq, [], W.Batch([]), [])
+        self.caches = [(poisoned_cache(self.shape_w, device), poisoned_cache(self.shape_w, device))
+                       for _ in range(num_layers)]
+        ws = B.paged_attn_decode_workspace_size(512, num_q_heads, num_kv_heads, head_dim,
+                                                max_blocks_per_seq * W.BLOCK_SIZE)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.scale = self.shape_w.scale
+
+    def values(self, step_index: int, layer: int, rows: int):
+        from workloads.sched import step_stream
+        s = step_stream(step_index, layer)
+        q = W.randn_bf16(self.seed, s, W.TAG_Q, (rows, self.hq, self.d), self.device)
+        k = W.randn_bf16(self.seed, s, W.TAG_K, (rows, self.hkv, self.d), self.device)
+        v = W.randn_bf16(self.seed, s, W.TAG_V, (rows, self.hkv, self.d), self.device)
+        return q, k, v
+
+    def run(self, steps, keep=None):
+        """keep: {step index: layers} whose attention outputs are returned
+        (on the host) as {(step index, layer): tensor}."""
+        kept = {}
+        for st in steps:
+            b = st.batch
+            m = B.pkv_prepare_step([s.seq_len for s in b.seqs], [s.num_cached for s in b.seqs],
+                                   [s.block_table for s in b.seqs], W.BLOCK_SIZE, self.mb, b.num_pad)
+            dm = DeviceMeta(m, self.device)
+            for layer in range(self.L):
+                q, k, v = self.values(st.index, layer, m.num_tokens)
+                kc, vc = self.caches[layer]
+                B.kv_store(k, v, kc, vc, dm.slot_mapping)
+                out = torch.empty_like(q)
+                if st.kind == "decode":
+                    B.paged_attn_decode(out, q, kc, vc, dm.block_tables, dm.context_lens, self.scale,
+                                        dm.max_context_len, self.workspace)
+                else:
+                    B.paged_attn_prefill_varlen(out, q, dm.cu_seqlens_q, dm.context_lens, kc, vc,
+                                                dm.block_tables, dm.max_q_len, dm.max_context_len, self.scale)
+                if keep and layer in keep.get(st.index, ()):
+                    kept[(st.index, layer)] = out.cpu()
+        return kept

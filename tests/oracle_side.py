@@ -110,3 +110,31 @@ def decode_sampled(w: W.Workload, idx, device="cpu") -> np.ndarray:
     ctx = np.asarray([step.seqs[b].seq_len for b in idx], dtype=np.int32)
     q = bits(q_all[list(idx)])
     return op.decode_ref(q, kc, vc, bt, ctx, w.scale)
+
+
+def trace_check(runner, steps, kept, layers, device="cuda"):
+    """Mirror ``layers`` of a scheduler-trace replay on the host with the
+    oracle's own metadata and in-place store, and compare the outputs the GPU
+    kept at sampled steps. Returns the number of (step, layer) checks made."""
+    from tests.test_gpu_parity import assert_close
+    shape = (runner.shape_w.num_blocks, runner.shape_w.block_size, runner.hkv, runner.d)
+    mirror = {l: (np.full(shape, NAN_BF16, dtype=np.uint16), np.full(shape, NAN_BF16, dtype=np.uint16))
+              for l in layers}
+    checked = 0
+    for st in steps:
+        b = st.batch
+        slots, cu, ctx, bt = op.prepare_step_ref([s.seq_len for s in b.seqs], [s.num_cached for s in b.seqs],
+                                                 [s.block_table for s in b.seqs], runner.shape_w.block_size,
+                                                 runner.mb, b.num_pad)
+        for l in layers:
+            q, k, v = runner.values(st.index, l, len(slots))
+            kc, vc = mirror[l]
+            op.kv_store_inplace_ref(kc, vc, bits(k), bits(v), slots)
+            if (st.index, l) in kept:
+                if st.kind == "decode":
+                    ref = op.decode_ref(bits(q), kc, vc, bt, ctx, runner.scale)
+                else:
+                    ref = op.prefill_ref(bits(q), cu, ctx, kc, vc, bt, runner.scale)
+                assert_close(kept[(st.index, l)], ref, cu, f"trace step {st.index} ({st.kind}) layer {l}")
+                checked += 1
+    return checked

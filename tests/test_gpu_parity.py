@@ -252,3 +252,28 @@ def test_empty_calls_are_noops():
     P.kv_store(z, z, dw.k_cache, dw.v_cache, torch.empty(0, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert (dw.k_cache.view(torch.int16) == H.NAN_BF16).all()
+
+
+# ----------------------------------------------------------------------------
+# configuration 5: scheduler-trace replay over 28 layers
+# ----------------------------------------------------------------------------
+
+def test_scheduler_trace_replay():
+    """Full replay (every step, all 28 layers) on the GPU; layers 0 and 27
+    mirrored on the host and compared at sampled steps: the first prefill,
+    the re-prefill after the first preemption, and decode steps including
+    the one that preempted, a middle one and the last."""
+    from workloads import sched as S
+    steps, reqs, _ = S.replay()
+    pre_idx = next(st.index for st in steps if st.preempted)
+    reprefill = next(st.index for st in steps[pre_idx:] if st.kind == "prefill")
+    dec = [st.index for st in steps if st.kind == "decode"]
+    sample = sorted({0, reprefill, dec[0], pre_idx, dec[len(dec) // 2], dec[-1]})
+    layers = (0, S.NUM_LAYERS - 1)
+    runner = H.TraceRunner(W.SEEDS[5], S.NUM_LAYERS, S.POOL_BLOCKS)
+    kept = runner.run(steps, keep={i: layers for i in sample})
+    torch.cuda.synchronize()
+    n = O.trace_check(runner, steps, kept, layers)
+    assert n == len(sample) * len(layers)
+    del runner
+    torch.cuda.empty_cache()
