@@ -57,7 +57,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -192,6 +192,15 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
  *   block_tables     device int32 [num_seqs, block_table_stride]
  *   max_q_len        host upper bound on n_s (sizes the launch)
  *   max_context_len  host upper bound on L_s
+ *   work_items       device int32 [num_work_items, 2] written by
+ *                    pkv_prefill_plan for these same cu_seqlens_q,
+ *                    context_lens and head counts (then one work-group per
+ *                    item), or NULL (then a (num_kv_heads, num_seqs,
+ *                    ceil(max_q_len / (128 / G))) grid whose work-groups past
+ *                    a sequence's last tile exit at once). 8-byte aligned.
+ *                    Items naming a sequence, head or tile that does not
+ *                    exist are skipped. Both launches give identical bits.
+ *   num_work_items   number of items (the plan's out_num_items)
  * Supported shapes as for paged_attn_decode. Deterministic.
  */
 pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,
@@ -201,7 +210,34 @@ pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu
                                      int32_t max_q_len, int32_t max_context_len,
                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                      int32_t block_size, int64_t num_blocks, float scale,
+                                     const int32_t* work_items, int32_t num_work_items,
                                      void* stream);
+
+/*
+ * pkv_prefill_plan — host-side work list for paged_attn_prefill_varlen.
+ *
+ * Part of the host step preparation (P1, "第五站：执行准备与 KV 容量": the
+ * step's cu_seqlens and context lengths are built on the host before the
+ * upload). One item per (sequence s, query tile t, KV head g) with at least
+ * one query token, where a tile holds 128 / G consecutive query tokens
+ * (G = num_q_heads / num_kv_heads). Item = {s, (t << 8) | g}. Items are
+ * sorted by the number of 64-key tiles they read, ceil((c_s + end_t) / 64)
+ * with end_t the tile's last query token + 1, largest first; equal costs
+ * keep the order (sequence, later tile first, KV head).
+ *
+ *   cu_seqlens_q, context_lens  host int32, as for paged_attn_prefill_varlen
+ *   out_items        host int32 [capacity, 2], or NULL to query the count
+ *   capacity         items out_items can hold
+ *   out_num_items    host int64 (written): number of items
+ * Errors: PKV_ERR_INVALID for a malformed batch (cu_seqlens_q[0] != 0, a
+ * decreasing cu_seqlens_q, a context shorter than its query run) or
+ * capacity too small; PKV_ERR_UNSUPPORTED for head counts the prefill
+ * kernel does not take. Nothing is written on error except the count.
+ */
+pkv_status pkv_prefill_plan(int32_t num_seqs, const int32_t* cu_seqlens_q,
+                            const int32_t* context_lens, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t* out_items, int64_t capacity,
+                            int64_t* out_num_items);
 
 #ifdef __cplusplus
 }

@@ -18,5 +18,7 @@ from .binding import (  # noqa: F401
     paged_attn_decode,
     paged_attn_decode_workspace_size,
     paged_attn_prefill_varlen,
+    pkv_prefill_plan,
     pkv_prepare_step,
+    prefill_plan_capacity,
 )

@@ -20,7 +20,9 @@ PKV_OK = 0
 STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "HIP", 4: "WORKSPACE"}
 
 EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
-           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_varlen")
+           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_varlen",
+           "pkv_prefill_plan")
+ABI_VERSION = 2
 
 
 class PkvError(RuntimeError):
@@ -62,8 +64,11 @@ def load_library(path: str = LIB_PATH):
                                       c_i64, c_f32, c_i32, c_vp, c_size, c_vp]
     lib.paged_attn_prefill_varlen.restype = c_i32
     lib.paged_attn_prefill_varlen.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
-                                              c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_f32, c_vp]
-    if lib.pkv_abi_version() != 1:
+                                              c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_f32, c_vp, c_i32,
+                                              c_vp]
+    lib.pkv_prefill_plan.restype = c_i32
+    lib.pkv_prefill_plan.argtypes = [c_i32, P_I32, P_I32, c_i32, c_i32, P_I32, c_i64, P_I64]
+    if lib.pkv_abi_version() != ABI_VERSION:
         raise RuntimeError("libpkv.so ABI version mismatch")
     _lib = lib
     return lib
@@ -133,6 +138,37 @@ def pkv_prepare_step(seq_lens, num_cached, block_tables, block_size: int, max_bl
     n = nt.value
     return StepMeta(slots[:n], cu[:rows + 1], ctx[:rows], bt[:rows * max_blocks_per_seq].reshape(rows, max_blocks_per_seq),
                     n, mq.value, mc.value)
+
+
+def pkv_prefill_plan(cu_seqlens_q, context_lens, num_q_heads: int, num_kv_heads: int, out=None) -> np.ndarray:
+    """Call ``pkv_prefill_plan`` on host arrays; returns int32 [n, 2] items.
+    ``out`` may be a preallocated host int32 array of 2 * capacity elements
+    (e.g. a pinned buffer); the result is then a view of it."""
+    lib = load_library()
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = cu.size - 1
+    if S < 0 or ctx.size < S:
+        raise ValueError("cu_seqlens_q / context_lens do not describe a batch")
+    n = ctypes.c_int64(0)
+    if out is None:
+        st = lib.pkv_prefill_plan(S, _i32p(cu), _i32p(ctx), int(num_q_heads), int(num_kv_heads), None, 0,
+                                  ctypes.byref(n))
+        _check("pkv_prefill_plan", st)
+        out = np.empty(max(2 * n.value, 2), dtype=np.int32)
+    if out.dtype != np.int32 or not out.flags.c_contiguous:
+        raise ValueError("out must be a contiguous int32 array")
+    st = lib.pkv_prefill_plan(S, _i32p(cu), _i32p(ctx), int(num_q_heads), int(num_kv_heads), _i32p(out),
+                              out.size // 2, ctypes.byref(n))
+    _check("pkv_prefill_plan", st)
+    return out[:2 * n.value].reshape(n.value, 2)
+
+
+def prefill_plan_capacity(total_q: int, num_seqs: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """Upper bound on the plan's item count for any batch of ``num_seqs``
+    sequences with ``total_q`` query tokens in all."""
+    tok = 128 // (num_q_heads // num_kv_heads)
+    return num_kv_heads * (total_q // tok + num_seqs)
 
 
 # ----------------------------------------------------------------------------
@@ -209,9 +245,10 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
 
 
 def paged_attn_prefill_varlen(out, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables, max_q_len,
-                              max_context_len, scale, stream=None):
+                              max_context_len, scale, work_items=None, stream=None):
     """out/q [T, H_q, D] bf16; cu_seqlens_q [S+1]; context_lens [S];
-    block_tables [S, stride] int32."""
+    block_tables [S, stride] int32; work_items: device int32 [n, 2] from
+    ``pkv_prefill_plan`` for the same batch, or None for the full grid."""
     torch = _torch()
     lib = load_library()
     T, Hq, D = q.shape
@@ -221,6 +258,11 @@ def paged_attn_prefill_varlen(out, q, cu_seqlens_q, context_lens, k_cache, v_cac
         raise ValueError("out must match q")
     if block_tables.dim() != 2 or block_tables.shape[0] < S or context_lens.shape[0] < S:
         raise ValueError("block_tables / context_lens do not cover the batch")
+    wi_ptr, wi_n = None, 0
+    if work_items is not None:
+        if work_items.dim() != 2 or work_items.shape[1] != 2:
+            raise ValueError("work_items must be [n, 2]")
+        wi_ptr, wi_n = _dev(work_items, "work_items", torch.int32), work_items.shape[0]
     st = lib.paged_attn_prefill_varlen(_dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
                                        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
                                        _dev(context_lens, "context_lens", torch.int32),
@@ -228,5 +270,5 @@ def paged_attn_prefill_varlen(out, q, cu_seqlens_q, context_lens, k_cache, v_cac
                                        _dev(v_cache, "v_cache", torch.bfloat16),
                                        _dev(block_tables, "block_tables", torch.int32), block_tables.stride(0), S,
                                        T, int(max_q_len), int(max_context_len), Hq, Hkv, D, B, N, float(scale),
-                                       _stream(stream))
+                                       wi_ptr, int(wi_n), _stream(stream))
     _check("paged_attn_prefill_varlen", st)

@@ -5,7 +5,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
+#include <vector>
 
 #include "common.h"
 
@@ -113,5 +115,69 @@ extern "C" pkv_status pkv_prepare_step(int32_t num_seqs, const int32_t* seq_lens
   if (out_num_tokens) *out_num_tokens = t;
   if (out_max_q) *out_max_q = max_q;
   if (out_max_ctx) *out_max_ctx = max_ctx;
+  return pkv::ok();
+}
+
+// Prefill work list: one item per (sequence, query tile, KV head) that holds
+// at least one query token, heaviest first. An item's cost is the number of
+// 64-key tiles it reads (its last query sits at c + tile_end - 1), so the
+// long items start first and the short ones fill the tail of the launch.
+// Within equal cost the order is sequence, later tile first, KV head, which
+// keeps the KV heads of one (sequence, tile) adjacent: with round-robin
+// dispatch over the XCDs every tile of one KV head then meets the same L2.
+extern "C" pkv_status pkv_prefill_plan(int32_t num_seqs, const int32_t* cu_seqlens_q,
+                                       const int32_t* context_lens, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t* out_items, int64_t capacity,
+                                       int64_t* out_num_items) {
+  using pkv::fail;
+  if (num_seqs < 0 || capacity < 0) return fail(PKV_ERR_INVALID, "pkv_prefill_plan: negative size");
+  if (!out_num_items) return fail(PKV_ERR_INVALID, "pkv_prefill_plan: null out_num_items");
+  if (num_kv_heads < 1 || num_kv_heads > 64 || num_q_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_prefill_plan: head counts %d/%d unsupported", num_q_heads, num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "pkv_prefill_plan: %d query heads per KV head (1, 2, 4 or 8)", G);
+  if (num_seqs > 0 && (!cu_seqlens_q || !context_lens))
+    return fail(PKV_ERR_INVALID, "pkv_prefill_plan: null input pointer");
+  const int tok_wg = 128 / G;  // query tokens per work-group of the prefill kernel
+  int64_t count = 0;
+  if (num_seqs > 0 && cu_seqlens_q[0] != 0) return fail(PKV_ERR_INVALID, "pkv_prefill_plan: cu_seqlens_q[0] != 0");
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = (int64_t)cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+    const int64_t L = context_lens[s];
+    if (n < 0) return fail(PKV_ERR_INVALID, "pkv_prefill_plan: cu_seqlens_q decreases at %d", s);
+    if (L < n) return fail(PKV_ERR_INVALID, "pkv_prefill_plan: seq %d context %lld < %lld query tokens", s,
+                           (long long)L, (long long)n);
+    if (n > ((int64_t)1 << 23) * tok_wg)
+      return fail(PKV_ERR_UNSUPPORTED, "pkv_prefill_plan: seq %d has more than 2^23 query tiles", s);
+    count += ((n + tok_wg - 1) / tok_wg) * num_kv_heads;
+  }
+  if (count > INT32_MAX) return fail(PKV_ERR_INVALID, "pkv_prefill_plan: more than 2^31 - 1 items");
+  *out_num_items = count;
+  if (!out_items) return pkv::ok();  // size query
+  if (count > capacity)
+    return fail(PKV_ERR_INVALID, "pkv_prefill_plan: %lld items, capacity %lld", (long long)count,
+                (long long)capacity);
+  struct Tile {
+    int64_t cost;
+    int32_t seq, tile;
+  };
+  std::vector<Tile> tiles;
+  tiles.reserve(count / num_kv_heads);
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = (int64_t)cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+    const int64_t c = context_lens[s] - n;
+    for (int64_t t = (n + tok_wg - 1) / tok_wg - 1; t >= 0; --t) {
+      const int64_t end = (t + 1) * tok_wg < n ? (t + 1) * tok_wg : n;
+      tiles.push_back({(c + end + 63) / 64, s, (int32_t)t});
+    }
+  }
+  std::stable_sort(tiles.begin(), tiles.end(), [](const Tile& x, const Tile& y) { return x.cost > y.cost; });
+  int64_t at = 0;
+  for (const Tile& t : tiles)
+    for (int32_t g = 0; g < num_kv_heads; ++g, ++at) {
+      out_items[2 * at] = t.seq;
+      out_items[2 * at + 1] = (t.tile << 8) | g;
+    }
   return pkv::ok();
 }

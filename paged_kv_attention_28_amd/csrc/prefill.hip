@@ -11,10 +11,13 @@
 //  * Work-group = 4 wavefronts on 128 (token, head) rows of one sequence and
 //    one KV head: 128 / G query tokens x the G query heads sharing that KV
 //    head, so each K/V tile staged in LDS serves every one of them.
-//  * Grid (kv_head, seq, q-tile counted from the end). kv_head is fastest, so
-//    (with round-robin dispatch over the 8 XCDs) all tiles of one KV head
-//    land on one XCD and share its L2; the last (longest) q-tiles of every
-//    sequence are dispatched first.
+//  * Work items come from a host plan (pkv_prefill_plan): one per non-empty
+//    (sequence, q-tile, kv_head), longest first, KV heads of a tile adjacent,
+//    so no work-group is launched for nothing, the short tiles fill the tail,
+//    and (with round-robin dispatch over the 8 XCDs) all tiles of one KV head
+//    land on one XCD and share its L2. Without a plan the grid is (kv_head,
+//    seq, q-tile counted from the end), sized by max_q_len, and work-groups
+//    past a sequence's last tile exit at once.
 //  * Per 64-key tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows
 //    from LDS, B = the wavefront's 32 query rows held in registers). In the
 //    transposed product each lane holds 32 scores of one query row, so the
@@ -121,14 +124,25 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
     const int32_t* __restrict__ context_lens, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int bt_stride, int hq, int hkv, int64_t num_blocks,
-    float scale_log2, int max_q, int max_ctx) {
+    float scale_log2, int max_q, int max_ctx, const int2* __restrict__ items, int num_seqs) {
   constexpr int kTokWG = 128 / G;  // query tokens per work-group
   constexpr int kTokW = 32 / G;    // per wavefront
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBufElems];
 
-  const int g = blockIdx.x;
-  const int b = blockIdx.y;
-  const int zt = blockIdx.z;
+  // work item: from the host plan (one per non-empty tile, heaviest first),
+  // else from the grid (kv_head, seq, q-tile counted from the end)
+  int g, b, tile;
+  if (items) {
+    const int2 it = items[blockIdx.x];
+    b = it.x;
+    g = it.y & 255;
+    tile = it.y >> 8;
+    if (b < 0 || b >= num_seqs || g >= hkv || tile < 0) return;
+  } else {
+    g = blockIdx.x;
+    b = blockIdx.y;
+    tile = -1 - (int)blockIdx.z;  // resolved once the tile count is known
+  }
   const int q0 = cu_seqlens_q[b];
   int n = cu_seqlens_q[b + 1] - q0;
   n = n > max_q ? max_q : n;
@@ -137,8 +151,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
   const int c = L - n;
   if (n <= 0 || c < 0) return;
   const int ntiles = (n + kTokWG - 1) / kTokWG;
-  if (zt >= ntiles) return;
-  const int tok_begin = (ntiles - 1 - zt) * kTokWG;
+  if (tile < 0) tile += ntiles;
+  if (tile < 0 || tile >= ntiles) return;
+  const int tok_begin = tile * kTokWG;
   const int tok_end = tok_begin + kTokWG < n ? tok_begin + kTokWG : n;
   const int kv_end = c + tok_end;
   const int nkt = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
@@ -325,7 +340,8 @@ extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const 
                                                 int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
                                                 int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                                int64_t num_blocks, float scale, void* stream) {
+                                                int64_t num_blocks, float scale, const int32_t* work_items,
+                                                int32_t num_work_items, void* stream) {
   using namespace pkv;
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0 || num_blocks < 0 ||
       block_table_stride < 0)
@@ -344,7 +360,10 @@ extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const 
     return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: scale must be finite and > 0");
   if (max_q_len > max_context_len)
     return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: max_q_len > max_context_len");
-  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (num_work_items < 0) return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: num_work_items < 0");
+  if (work_items && (reinterpret_cast<uintptr_t>(work_items) & 7))
+    return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: work_items must be 8-byte aligned");
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0 || (work_items && num_work_items == 0)) return ok();
   if (!out || !q || !cu_seqlens_q || !context_lens || !k_cache || !v_cache || !block_tables)
     return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: null pointer");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -359,7 +378,8 @@ extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const 
   if (ztiles > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_varlen: max_q_len too large");
   const float scale_log2 = scale * 1.4426950408889634f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  dim3 grid(num_kv_heads, num_seqs, ztiles);
+  const dim3 grid = work_items ? dim3(num_work_items) : dim3(num_kv_heads, num_seqs, ztiles);
+  const int2* items = reinterpret_cast<const int2*>(work_items);
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const char* kc = static_cast<const char*>(k_cache);
@@ -367,7 +387,7 @@ extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const 
 #define PKV_PREFILL_LAUNCH(GG)                                                                                  \
   hipLaunchKernelGGL(prefill_kernel<GG>, grid, dim3(256), 0, s, o, qq, cu_seqlens_q, context_lens, kc, vc,      \
                      block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2,      \
-                     max_q_len, max_context_len)
+                     max_q_len, max_context_len, items, num_seqs)
   switch (G) {
     case 1: PKV_PREFILL_LAUNCH(1); break;
     case 2: PKV_PREFILL_LAUNCH(2); break;

@@ -32,9 +32,10 @@ def meta(w: W.Workload, batch: W.Batch, out=None) -> B.StepMeta:
 
 
 class DeviceMeta:
-    """Device copies of one batch's metadata."""
+    """Device copies of one batch's metadata; with ``heads`` = (H_q, H_kv)
+    also the prefill work plan built from it on the host."""
 
-    def __init__(self, m: B.StepMeta, device="cuda"):
+    def __init__(self, m: B.StepMeta, device="cuda", heads=None):
         self.host = m
         self.slot_mapping = torch.from_numpy(np.ascontiguousarray(m.slot_mapping)).to(device)
         self.cu_seqlens_q = torch.from_numpy(np.ascontiguousarray(m.cu_seqlens_q)).to(device)
@@ -43,6 +44,10 @@ class DeviceMeta:
         self.max_q_len = m.max_q_len
         self.max_context_len = m.max_context_len
         self.num_tokens = m.num_tokens
+        self.work_items = None
+        if heads is not None:
+            plan = B.pkv_prefill_plan(m.cu_seqlens_q, m.context_lens, heads[0], heads[1])
+            self.work_items = torch.from_numpy(np.ascontiguousarray(plan)).to(device)
 
 
 class DeviceWorkload:
@@ -80,9 +85,11 @@ class DeviceWorkload:
     # -- attention -----------------------------------------------------------
     def pass_inputs(self, p: W.Pass):
         q = W.pass_q(self.w, p, self.device)
-        return q, DeviceMeta(meta(self.w, p.batch), self.device)
+        heads = (self.w.num_q_heads, self.w.num_kv_heads) if p.kind == "prefill" else None
+        return q, DeviceMeta(meta(self.w, p.batch), self.device, heads)
 
-    def run_pass(self, p: W.Pass, q=None, m: DeviceMeta = None, out=None, workspace=None):
+    def run_pass(self, p: W.Pass, q=None, m: DeviceMeta = None, out=None, workspace=None, plan=True):
+        """plan=False runs prefill on the full grid instead of the host plan."""
         if q is None or m is None:
             q, m = self.pass_inputs(p)
         if out is None:
@@ -94,7 +101,8 @@ class DeviceWorkload:
                                 m.max_context_len, workspace)
         else:
             B.paged_attn_prefill_varlen(out, q, m.cu_seqlens_q, m.context_lens, self.k_cache, self.v_cache,
-                                        m.block_tables, m.max_q_len, m.max_context_len, self.w.scale)
+                                        m.block_tables, m.max_q_len, m.max_context_len, self.w.scale,
+                                        work_items=m.work_items if plan else None)
         return out
 
 
@@ -120,8 +128,12 @@ class StepRunner:
         m0 = meta(w, p.batch)
         rows = len(p.batch.seqs) + p.batch.num_pad
         # one int32 buffer holds slot mapping | cu_seqlens_q | context lens |
-        # block tables, so a step uploads its metadata with a single copy
-        self.shapes = (m0.num_tokens, rows + 1, rows, rows * w.max_blocks_per_seq)
+        # block tables | prefill plan, so a step uploads its metadata with a
+        # single copy (the plan starts at an even offset: 8-byte items)
+        cap = B.prefill_plan_capacity(m0.num_tokens, rows, w.num_q_heads, w.num_kv_heads)
+        head = m0.num_tokens + 2 * rows + 1 + rows * w.max_blocks_per_seq
+        self.shapes = (m0.num_tokens, rows + 1, rows, rows * w.max_blocks_per_seq, head & 1,
+                       2 * cap if p.kind == "prefill" else 0)
         offs = np.concatenate([[0], np.cumsum(self.shapes)]).astype(np.int64)
         self.offs = offs
         total = int(offs[-1])
@@ -129,6 +141,8 @@ class StepRunner:
         self.events = [None, None]
         self.dev_flat = torch.empty(total, dtype=torch.int32, device=dev)
         self.dev_meta = tuple(self.dev_flat[offs[i]:offs[i + 1]] for i in range(4))
+        self.dev_plan = self.dev_flat[offs[5]:offs[6]]
+        self.num_items = 0
         self.max_q_len = m0.max_q_len
         self.max_ctx = m0.max_context_len
         self.workspace = (decode_workspace(w, rows, self.max_ctx, dev) if p.kind == "decode" else None)
@@ -142,7 +156,10 @@ class StepRunner:
             self.events[k].synchronize()
         flat = self.pinned[k].numpy()
         o = self.offs
-        meta(w, p.batch, out=tuple(flat[o[i]:o[i + 1]] for i in range(4)))
+        m = meta(w, p.batch, out=tuple(flat[o[i]:o[i + 1]] for i in range(4)))
+        if p.kind == "prefill":
+            self.num_items = B.pkv_prefill_plan(m.cu_seqlens_q, m.context_lens, w.num_q_heads, w.num_kv_heads,
+                                                out=flat[o[5]:o[6]]).shape[0]
         self.dev_flat.copy_(self.pinned[k], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()
@@ -160,8 +177,9 @@ class StepRunner:
             B.paged_attn_decode(self.out, self.q, self.dw.k_cache, self.dw.v_cache, bt2, ctx, w.scale,
                                 self.max_ctx, self.workspace)
         else:
+            items = self.dev_plan[:2 * self.num_items].view(self.num_items, 2)
             B.paged_attn_prefill_varlen(self.out, self.q, cu, ctx, self.dw.k_cache, self.dw.v_cache, bt2,
-                                        self.max_q_len, self.max_ctx, w.scale)
+                                        self.max_q_len, self.max_ctx, w.scale, work_items=items)
 
     def kernels(self):
         self.store_only()
@@ -207,7 +225,7 @@ class TraceRunner:
             b = st.batch
             m = B.pkv_prepare_step([s.seq_len for s in b.seqs], [s.num_cached for s in b.seqs],
                                    [s.block_table for s in b.seqs], W.BLOCK_SIZE, self.mb, b.num_pad)
-            dm = DeviceMeta(m, self.device)
+            dm = DeviceMeta(m, self.device, (self.hq, self.hkv) if st.kind == "prefill" else None)
             for layer in range(self.L):
                 q, k, v = self.values(st.index, layer, m.num_tokens)
                 kc, vc = self.caches[layer]
@@ -218,7 +236,8 @@ class TraceRunner:
                                         dm.max_context_len, self.workspace)
                 else:
                     B.paged_attn_prefill_varlen(out, q, dm.cu_seqlens_q, dm.context_lens, kc, vc,
-                                                dm.block_tables, dm.max_q_len, dm.max_context_len, self.scale)
+                                                dm.block_tables, dm.max_q_len, dm.max_context_len, self.scale,
+                                                work_items=dm.work_items)
                 if keep and layer in keep.get(st.index, ()):
                     kept[(st.index, layer)] = out.cpu()
         return kept

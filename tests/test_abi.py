@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(P.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
 
 
 def test_product_package_does_not_import_oracle():
@@ -157,9 +157,84 @@ def test_decode_validation(lib):
 def test_prefill_validation(lib):
     args = lambda **kw: [F, F, F, F, F, F, F, kw.get("bts", 8), kw.get("S", 4), kw.get("T", 100),
                          kw.get("maxq", 64), kw.get("maxctx", 2048), kw.get("hq", 16), 8, kw.get("d", 128), 256,
-                         100, 0.088, None]
+                         100, 0.088, kw.get("wi", None), kw.get("nwi", 0), None]
     assert lib.paged_attn_prefill_varlen(*args(d=256)) == 2
     assert lib.paged_attn_prefill_varlen(*args(hq=40)) == 2
     assert lib.paged_attn_prefill_varlen(*args(maxq=4096)) == 1   # max_q > max_ctx
     assert lib.paged_attn_prefill_varlen(*args(bts=2)) == 1
     assert lib.paged_attn_prefill_varlen(*args(T=0)) == 0
+    assert lib.paged_attn_prefill_varlen(*args(wi=F, nwi=-1)) == 1   # negative item count
+    assert lib.paged_attn_prefill_varlen(*args(wi=F + 4, nwi=8)) == 1  # items not 8-byte aligned
+    assert lib.paged_attn_prefill_varlen(*args(wi=F, nwi=0)) == 0    # empty plan: nothing to do
+
+
+# ----------------------------------------------------------------------------
+# prefill work plan (host logic, checked against its definition)
+# ----------------------------------------------------------------------------
+
+def _plan_expected(cu, ctx, hq, hkv):
+    """Every (seq, tile, head) with a query token, ordered by the number of
+    64-key tiles read (descending), then seq, later tile first, head."""
+    tok = 128 // (hq // hkv)
+    keys = []
+    for s in range(len(cu) - 1):
+        n = cu[s + 1] - cu[s]
+        c = ctx[s] - n
+        for t in range(-(-n // tok)):
+            end = min((t + 1) * tok, n)
+            cost = -(-(c + end) // 64)
+            for g in range(hkv):
+                keys.append(((-cost, s, -t, g), (s, (t << 8) | g)))
+    keys.sort()
+    return np.array([k[1] for k in keys], dtype=np.int32).reshape(-1, 2)
+
+
+def _plan_batches():
+    rng = np.random.default_rng(7)
+    out = []
+    for w in (W.make(1), W.make(3)):
+        m = P.pkv_prepare_step([s.seq_len for s in w.passes[0].batch.seqs],
+                               [s.num_cached for s in w.passes[0].batch.seqs],
+                               [s.block_table for s in w.passes[0].batch.seqs], w.block_size,
+                               w.max_blocks_per_seq, w.passes[0].batch.num_pad)
+        out.append((m.cu_seqlens_q, m.context_lens, w.num_q_heads, w.num_kv_heads))
+    for hq, hkv in ((8, 8), (16, 8), (32, 8), (64, 8), (4, 1), (16, 2)):
+        n = rng.integers(0, 700, size=int(rng.integers(1, 12)))
+        c = rng.integers(0, 900, size=n.size)
+        cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+        out.append((cu, (n + c).astype(np.int32), hq, hkv))
+    return out
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_prefill_plan_matches_definition(i):
+    cu, ctx, hq, hkv = _plan_batches()[i]
+    got = P.pkv_prefill_plan(cu, ctx, hq, hkv)
+    want = _plan_expected([int(x) for x in cu], [int(x) for x in ctx], hq, hkv)
+    np.testing.assert_array_equal(got, want.reshape(got.shape))
+    assert got.shape[0] <= P.prefill_plan_capacity(int(cu[-1]), len(cu) - 1, hq, hkv)
+    if hkv == 8 and got.size:
+        # KV heads of one (seq, tile) stay adjacent, so item i serves head i % 8
+        np.testing.assert_array_equal(got[:, 1] & 255, np.arange(got.shape[0]) % 8)
+
+
+def test_prefill_plan_validation(lib):
+    n = ctypes.c_int64(-5)
+    cu = np.array([0, 10, 5], dtype=np.int32)
+    ctx = np.array([10, 10], dtype=np.int32)
+    p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    assert lib.pkv_prefill_plan(2, p32(cu), p32(ctx), 16, 8, None, 0, ctypes.byref(n)) == 1   # decreasing
+    cu = np.array([1, 10], dtype=np.int32)
+    assert lib.pkv_prefill_plan(1, p32(cu), p32(ctx), 16, 8, None, 0, ctypes.byref(n)) == 1   # cu[0] != 0
+    cu = np.array([0, 20], dtype=np.int32)
+    assert lib.pkv_prefill_plan(1, p32(cu), p32(ctx), 16, 8, None, 0, ctypes.byref(n)) == 1   # ctx < n
+    assert lib.pkv_prefill_plan(1, p32(cu), p32(ctx), 24, 8, None, 0, ctypes.byref(n)) == 2   # group of 3
+    cu = np.array([0, 10], dtype=np.int32)
+    assert lib.pkv_prefill_plan(1, p32(cu), p32(ctx), 16, 8, None, 0, ctypes.byref(n)) == 0
+    assert n.value == 8
+    items = np.full(16, -7, dtype=np.int32)
+    assert lib.pkv_prefill_plan(1, p32(cu), p32(ctx), 16, 8, p32(items), 7, ctypes.byref(n)) == 1  # capacity
+    assert (items == -7).all()
+    assert lib.pkv_prefill_plan(1, p32(cu), p32(ctx), 16, 8, p32(items), 8, ctypes.byref(n)) == 0
+    assert items.reshape(8, 2).tolist() == [[0, g] for g in range(8)]
+    assert lib.pkv_prefill_plan(0, None, None, 16, 8, None, 0, ctypes.byref(n)) == 0 and n.value == 0

@@ -101,6 +101,45 @@ def test_attention_deterministic(built, k):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("k", [2, 3])
+def test_step_runner_matches_pass(built, k):
+    """The launch the benchmark times (pinned metadata buffer, one upload,
+    store then attention, prefill on the host work plan) gives the same bits
+    as the separately prepared pass checked against the oracle above."""
+    w, dw, kc, vc = built(k)
+    p = w.passes[0]
+    q, m = dw.pass_inputs(p)
+    ref = dw.run_pass(p, q, m)
+    runner = H.StepRunner(dw, p)
+    for _ in range(3):
+        runner.step()
+    torch.cuda.synchronize()
+    assert torch.equal(runner.out.view(torch.int16), ref.view(torch.int16))
+    assert np.array_equal(_cache_bits(dw.k_cache), kc)
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_prefill_plan_and_grid_bit_identical(built, k):
+    """Prefill on the host work plan and on the full grid give the same bits;
+    plan items naming a sequence, head or tile that does not exist are
+    skipped."""
+    import paged_kv_attention_28_amd as P
+    w, dw, kc, vc = built(k)
+    p = next(x for x in w.passes if x.kind == "prefill")
+    q, m = dw.pass_inputs(p)
+    a = dw.run_pass(p, q, m, plan=True)
+    b = dw.run_pass(p, q, m, plan=False)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    S = len(m.host.cu_seqlens_q) - 1
+    bogus = torch.tensor([[S, 0], [S + 100, 0], [-1, 0], [0, w.num_kv_heads], [0, 255], [0, 1000 << 8],
+                          [0, -256]], dtype=torch.int32, device="cuda")
+    items = torch.cat([bogus[:3], m.work_items, bogus[3:]]).contiguous()
+    out = torch.empty_like(q)
+    P.paged_attn_prefill_varlen(out, q, m.cu_seqlens_q, m.context_lens, dw.k_cache, dw.v_cache, m.block_tables,
+                                m.max_q_len, m.max_context_len, w.scale, work_items=items)
+    assert torch.equal(out.view(torch.int16), a.view(torch.int16))
+
+
 # ----------------------------------------------------------------------------
 # configuration 4: full-size launch, sampled sequences checked one by one
 # ----------------------------------------------------------------------------
@@ -177,6 +216,9 @@ def test_edge_parity(name):
     out = dw.run_pass(p, q, m)
     ref = O.run_pass(w, p, kc, vc, q=q)
     assert_close(out, ref, m.host.cu_seqlens_q, name)
+    if p.kind == "prefill":
+        grid = dw.run_pass(p, q, m, plan=False)
+        assert torch.equal(grid.view(torch.int16), out.view(torch.int16)), "plan and grid launches differ"
     if name == "decode_len1":
         # a one-token context returns its V row exactly
         G = w.num_q_heads // w.num_kv_heads
