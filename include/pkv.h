@@ -30,8 +30,10 @@
  *     are skipped / read as masked), but results for such inputs are
  *     unspecified.
  *   - A call with zero work returns PKV_OK without launching.
- *   - The only global state is the thread-local error message: calls from
- *     different threads on different streams are independent.
+ *   - Global state: the thread-local error message and a mutex-guarded,
+ *     per-device cache of the decode kernel's resident work-group count.
+ *     Calls from different threads on different streams are independent; a
+ *     scheduler handle (pkv_sched) belongs to one thread at a time.
  */
 #ifndef PKV_H
 #define PKV_H
@@ -57,7 +59,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -238,6 +240,80 @@ pkv_status pkv_prefill_plan(int32_t num_seqs, const int32_t* cu_seqlens_q,
                             const int32_t* context_lens, int32_t num_q_heads,
                             int32_t num_kv_heads, int32_t* out_items, int64_t capacity,
                             int64_t* out_num_items);
+
+/*
+ * Native scheduler and block manager (host). A token-free engine loop: each
+ * step decides which sequences run and which cache blocks they own; the
+ * caller turns the batch into step metadata with pkv_prepare_step (and
+ * pkv_prefill_plan for a prefill step) and runs the kernels.
+ *
+ * P1, "第三站：调度器": prefill first, FCFS from the waiting queue within
+ * max_num_seqs, the token budget and the free blocks; only the first request
+ * of a step may be cut to the remaining budget (its remainder stays at the
+ * head of the queue); a step with any prefill runs no decode. Otherwise every
+ * running sequence advances one token and, when no block is free, the most
+ * recently added running sequences are preempted (their blocks freed, their
+ * requests back at the front of the queue, recomputed from position 0).
+ * P1, "第四站：块管理与前缀缓存": blocks for the whole current length on first
+ * scheduling, one more in decode exactly when len % block_size == 1, a FIFO
+ * free queue; prefix caching (token hashing) is not part of a token-free
+ * scheduler. P1, "第五站": decode batches are padded to the replay buckets
+ * 1, 2, 4, 8, then multiples of 16 up to 512. P1, "第一站：主循环": a
+ * completed prompt yields one token and each decode step one; a request
+ * finishes after output_len tokens (so it runs output_len - 1 decode steps).
+ * Freed blocks are appended in table order; within a decode step sequences
+ * are extended in running order; preemptions of a decode phase that leaves
+ * nothing to run are reported with the next recorded step.
+ *
+ * Usage: create; add requests; loop { schedule; (run the step); postprocess }
+ * until schedule returns kind PKV_STEP_NONE; destroy. Not thread-safe.
+ */
+typedef struct pkv_sched pkv_sched;
+
+enum { PKV_STEP_NONE = -1, PKV_STEP_DECODE = 0, PKV_STEP_PREFILL = 1 };
+
+typedef struct {
+  int32_t kind;            /* PKV_STEP_PREFILL, PKV_STEP_DECODE, or PKV_STEP_NONE when all requests finished */
+  int32_t num_seqs;        /* sequences in the batch */
+  int32_t num_pad;         /* decode: padding rows up to the replay bucket; prefill: 0 */
+  int32_t chunked_first;   /* prefill: the first sequence was cut to the remaining token budget */
+  int32_t num_preempted;   /* requests preempted since the previous recorded step */
+  const int32_t* request_ids;  /* [num_seqs] ids returned by pkv_sched_add */
+  const int32_t* seq_lens;     /* [num_seqs] sequence length once this step's tokens are in */
+  const int32_t* num_cached;   /* [num_seqs] tokens already in the cache (the step computes the rest) */
+  const int32_t* full_lens;    /* [num_seqs] prompt + generated tokens of the request */
+  const int64_t* bt_offsets;   /* [num_seqs + 1] CSR offsets into bt_data */
+  const int32_t* bt_data;      /* block tables, concatenated */
+  const int32_t* preempted;    /* [num_preempted] request ids */
+} pkv_sched_batch;
+
+/* New scheduler over a pool of num_blocks blocks (ids 0 .. num_blocks - 1).
+ * PKV_ERR_INVALID for non-positive sizes. The caller owns *out. */
+pkv_status pkv_sched_create(int32_t num_blocks, int32_t block_size, int32_t max_num_seqs,
+                            int32_t max_num_batched_tokens, pkv_sched** out);
+pkv_status pkv_sched_destroy(pkv_sched* s);
+
+/* Queue a request (prompt_len >= 1, output_len >= 1); *out_id (if non-NULL)
+ * gets its id, consecutive from 0. Not allowed between schedule and
+ * postprocess. */
+pkv_status pkv_sched_add(pkv_sched* s, int32_t prompt_len, int32_t output_len, int32_t* out_id);
+
+/* Decide the next step and describe it in *out. The arrays are owned by the
+ * scheduler and stay valid until the next call on it. PKV_ERR_INVALID if the
+ * previous step was not postprocessed, or if nothing can run because the
+ * request at the head of the queue needs more blocks than the pool holds. */
+pkv_status pkv_sched_schedule(pkv_sched* s, pkv_sched_batch* out);
+
+/* Apply the outcome of the scheduled step: prefill sequences advance by the
+ * tokens they computed (a completed prompt yields one token), decode
+ * sequences by one token; finished requests free their blocks. */
+pkv_status pkv_sched_postprocess(pkv_sched* s);
+
+/* Requests not finished yet (-1 for a NULL handle). */
+int32_t pkv_sched_unfinished(const pkv_sched* s);
+
+/* Blocks in the free queue (-1 for a NULL handle). */
+int32_t pkv_sched_free_blocks(const pkv_sched* s);
 
 #ifdef __cplusplus
 }

@@ -11,6 +11,8 @@ from .binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     PkvError,
+    SchedStep,
+    Scheduler,
     StepMeta,
     kv_store,
     last_error,

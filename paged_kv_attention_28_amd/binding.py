@@ -21,8 +21,9 @@ STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "HIP", 4: "WORKSPACE"}
 
 EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_varlen",
-           "pkv_prefill_plan")
-ABI_VERSION = 2
+           "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
+           "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks")
+ABI_VERSION = 3
 
 
 class PkvError(RuntimeError):
@@ -32,6 +33,16 @@ class PkvError(RuntimeError):
 
 
 _lib = None
+
+
+class SchedBatch(ctypes.Structure):
+    """pkv_sched_batch (include/pkv.h)."""
+    _fields_ = [("kind", ctypes.c_int32), ("num_seqs", ctypes.c_int32), ("num_pad", ctypes.c_int32),
+                ("chunked_first", ctypes.c_int32), ("num_preempted", ctypes.c_int32),
+                ("request_ids", ctypes.POINTER(ctypes.c_int32)), ("seq_lens", ctypes.POINTER(ctypes.c_int32)),
+                ("num_cached", ctypes.POINTER(ctypes.c_int32)), ("full_lens", ctypes.POINTER(ctypes.c_int32)),
+                ("bt_offsets", ctypes.POINTER(ctypes.c_int64)), ("bt_data", ctypes.POINTER(ctypes.c_int32)),
+                ("preempted", ctypes.POINTER(ctypes.c_int32))]
 
 c_i32, c_i64, c_f32, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 P_I32 = ctypes.POINTER(ctypes.c_int32)
@@ -68,6 +79,20 @@ def load_library(path: str = LIB_PATH):
                                               c_vp]
     lib.pkv_prefill_plan.restype = c_i32
     lib.pkv_prefill_plan.argtypes = [c_i32, P_I32, P_I32, c_i32, c_i32, P_I32, c_i64, P_I64]
+    lib.pkv_sched_create.restype = c_i32
+    lib.pkv_sched_create.argtypes = [c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]
+    lib.pkv_sched_destroy.restype = c_i32
+    lib.pkv_sched_destroy.argtypes = [c_vp]
+    lib.pkv_sched_add.restype = c_i32
+    lib.pkv_sched_add.argtypes = [c_vp, c_i32, c_i32, P_I32]
+    lib.pkv_sched_schedule.restype = c_i32
+    lib.pkv_sched_schedule.argtypes = [c_vp, ctypes.POINTER(SchedBatch)]
+    lib.pkv_sched_postprocess.restype = c_i32
+    lib.pkv_sched_postprocess.argtypes = [c_vp]
+    lib.pkv_sched_unfinished.restype = c_i32
+    lib.pkv_sched_unfinished.argtypes = [c_vp]
+    lib.pkv_sched_free_blocks.restype = c_i32
+    lib.pkv_sched_free_blocks.argtypes = [c_vp]
     if lib.pkv_abi_version() != ABI_VERSION:
         raise RuntimeError("libpkv.so ABI version mismatch")
     _lib = lib
@@ -169,6 +194,86 @@ def prefill_plan_capacity(total_q: int, num_seqs: int, num_q_heads: int, num_kv_
     sequences with ``total_q`` query tokens in all."""
     tok = 128 // (num_q_heads // num_kv_heads)
     return num_kv_heads * (total_q // tok + num_seqs)
+
+
+class SchedStep:
+    """One scheduled step, copied out of the scheduler's buffers."""
+
+    def __init__(self, kind, request_ids, seq_lens, num_cached, full_lens, block_tables, num_pad, chunked_first,
+                 preempted):
+        self.kind = kind                    # "prefill" or "decode"
+        self.request_ids = request_ids      # list of int
+        self.seq_lens = seq_lens
+        self.num_cached = num_cached
+        self.full_lens = full_lens
+        self.block_tables = block_tables    # list of lists of block ids
+        self.num_pad = num_pad
+        self.chunked_first = chunked_first
+        self.preempted = preempted
+
+
+class Scheduler:
+    """The native scheduler (``pkv_sched_*``): add requests, then
+    ``schedule()`` / ``postprocess()`` until ``schedule()`` returns None."""
+
+    def __init__(self, num_blocks: int, block_size: int, max_num_seqs: int, max_num_batched_tokens: int):
+        self._lib = load_library()
+        h = c_vp()
+        _check("pkv_sched_create", self._lib.pkv_sched_create(int(num_blocks), int(block_size), int(max_num_seqs),
+                                                              int(max_num_batched_tokens), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_sched_destroy(self._h)
+            self._h = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add(self, prompt_len: int, output_len: int) -> int:
+        rid = ctypes.c_int32(-1)
+        _check("pkv_sched_add", self._lib.pkv_sched_add(self._h, int(prompt_len), int(output_len), ctypes.byref(rid)))
+        return rid.value
+
+    def schedule(self):
+        b = SchedBatch()
+        _check("pkv_sched_schedule", self._lib.pkv_sched_schedule(self._h, ctypes.byref(b)))
+        if b.kind < 0:
+            return None
+        n = b.num_seqs
+        off = [b.bt_offsets[i] for i in range(n + 1)]
+        return SchedStep("prefill" if b.kind == 1 else "decode", [b.request_ids[i] for i in range(n)],
+                         [b.seq_lens[i] for i in range(n)], [b.num_cached[i] for i in range(n)],
+                         [b.full_lens[i] for i in range(n)],
+                         [[b.bt_data[j] for j in range(off[i], off[i + 1])] for i in range(n)], b.num_pad,
+                         bool(b.chunked_first), [b.preempted[i] for i in range(b.num_preempted)])
+
+    def postprocess(self):
+        _check("pkv_sched_postprocess", self._lib.pkv_sched_postprocess(self._h))
+
+    @property
+    def unfinished(self) -> int:
+        return self._lib.pkv_sched_unfinished(self._h)
+
+    @property
+    def free_blocks(self) -> int:
+        return self._lib.pkv_sched_free_blocks(self._h)
+
+    def run(self, prompts, outputs):
+        """Add the requests and run the schedule to completion; the list of steps."""
+        for p, o in zip(prompts, outputs):
+            self.add(p, o)
+        steps = []
+        while True:
+            st = self.schedule()
+            if st is None:
+                return steps
+            steps.append(st)
+            self.postprocess()
 
 
 # ----------------------------------------------------------------------------

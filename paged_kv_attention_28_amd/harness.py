@@ -191,10 +191,10 @@ class StepRunner:
 
 
 class TraceRunner:
-    """Replays a scheduler trace (configuration 5) over several layers: each
-    step prepares its metadata on the host once, then for every layer draws
-    fresh seeded q/k/v, stores the step's K/V into that layer's caches and
-    runs prefill or decode attention."""
+    """Replays the steps of the native scheduler (``binding.Scheduler``) over
+    several layers: each step prepares its metadata on the host once, then
+    for every layer draws fresh seeded q/k/v, stores the step's K/V into that
+    layer's caches and runs prefill or decode attention."""
 
     def __init__(self, seed: int, num_layers: int, num_blocks: int, max_blocks_per_seq: int = 8,
                  num_q_heads: int = 16, num_kv_heads: int = 8, head_dim: int = 128, device="cuda"):
@@ -218,16 +218,15 @@ class TraceRunner:
         return q, k, v
 
     def run(self, steps, keep=None):
-        """keep: {step index: layers} whose attention outputs are returned
-        (on the host) as {(step index, layer): tensor}."""
+        """steps: ``binding.SchedStep`` list (step i has index i). keep:
+        {step index: layers} whose attention outputs are returned (on the
+        host) as {(step index, layer): tensor}."""
         kept = {}
-        for st in steps:
-            b = st.batch
-            m = B.pkv_prepare_step([s.seq_len for s in b.seqs], [s.num_cached for s in b.seqs],
-                                   [s.block_table for s in b.seqs], W.BLOCK_SIZE, self.mb, b.num_pad)
+        for i, st in enumerate(steps):
+            m = B.pkv_prepare_step(st.seq_lens, st.num_cached, st.block_tables, W.BLOCK_SIZE, self.mb, st.num_pad)
             dm = DeviceMeta(m, self.device, (self.hq, self.hkv) if st.kind == "prefill" else None)
             for layer in range(self.L):
-                q, k, v = self.values(st.index, layer, m.num_tokens)
+                q, k, v = self.values(i, layer, m.num_tokens)
                 kc, vc = self.caches[layer]
                 B.kv_store(k, v, kc, vc, dm.slot_mapping)
                 out = torch.empty_like(q)
@@ -238,6 +237,6 @@ class TraceRunner:
                     B.paged_attn_prefill_varlen(out, q, dm.cu_seqlens_q, dm.context_lens, kc, vc,
                                                 dm.block_tables, dm.max_q_len, dm.max_context_len, self.scale,
                                                 work_items=dm.work_items)
-                if keep and layer in keep.get(st.index, ()):
-                    kept[(st.index, layer)] = out.cpu()
+                if keep and layer in keep.get(i, ()):
+                    kept[(i, layer)] = out.cpu()
         return kept

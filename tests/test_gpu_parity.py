@@ -301,19 +301,29 @@ def test_empty_calls_are_noops():
 # ----------------------------------------------------------------------------
 
 def test_scheduler_trace_replay():
-    """Full replay (every step, all 28 layers) on the GPU; layers 0 and 27
+    """The native scheduler's steps (identical to the oracle scheduler's,
+    checked first) replayed on the GPU for all 28 layers; layers 0 and 27
     mirrored on the host and compared at sampled steps: the first prefill,
     the re-prefill after the first preemption, and decode steps including
     the one that preempted, a middle one and the last."""
+    import paged_kv_attention_28_amd as P
+    from oracle import sched as OS
     from workloads import sched as S
-    steps, reqs, _ = S.replay()
+    prompts, outputs = S.requests()
+    steps, reqs, _ = OS.replay(prompts, outputs, S.POOL_BLOCKS, S.MAX_NUM_SEQS, S.MAX_BATCHED_TOKENS)
+    native = P.Scheduler(S.POOL_BLOCKS, W.BLOCK_SIZE, S.MAX_NUM_SEQS, S.MAX_BATCHED_TOKENS).run(prompts, outputs)
+    assert len(native) == len(steps)
+    for a, b in zip(native, steps):
+        assert (a.kind, a.request_ids, a.num_pad, a.preempted) == (b.kind, b.rids, b.batch.num_pad, b.preempted)
+        assert [(L, c, t) for L, c, t in zip(a.seq_lens, a.num_cached, a.block_tables)] == \
+               [(s.seq_len, s.num_cached, s.block_table) for s in b.batch.seqs]
     pre_idx = next(st.index for st in steps if st.preempted)
     reprefill = next(st.index for st in steps[pre_idx:] if st.kind == "prefill")
     dec = [st.index for st in steps if st.kind == "decode"]
     sample = sorted({0, reprefill, dec[0], pre_idx, dec[len(dec) // 2], dec[-1]})
     layers = (0, S.NUM_LAYERS - 1)
     runner = H.TraceRunner(W.SEEDS[5], S.NUM_LAYERS, S.POOL_BLOCKS)
-    kept = runner.run(steps, keep={i: layers for i in sample})
+    kept = runner.run(native, keep={i: layers for i in sample})
     torch.cuda.synchronize()
     n = O.trace_check(runner, steps, kept, layers)
     assert n == len(sample) * len(layers)

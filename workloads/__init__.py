@@ -18,7 +18,7 @@ Workloads (shapes follow a Qwen3-0.6B-like attention layer):
               carry a 256/512-token prefix in shared refcounted blocks; the
               first is a chunk continuation cut mid-block.
   4 long      512 sequences, context U[4096, 32768], 32 Q / 8 KV heads.
-  5 trace     FCFS prefill-first replay over 28 layers (``workloads.sched``).
+  5 trace     request lengths for the FCFS prefill-first replay over 28 layers (``workloads.sched``).
 """
 
 from __future__ import annotations
