@@ -59,7 +59,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 3
+#define PKV_ABI_VERSION 4
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -314,6 +314,61 @@ int32_t pkv_sched_unfinished(const pkv_sched* s);
 
 /* Blocks in the free queue (-1 for a NULL handle). */
 int32_t pkv_sched_free_blocks(const pkv_sched* s);
+
+/*
+ * Decode-step graphs. P1, "第五站：执行准备与 KV 容量" (CUDA Graph paragraph):
+ * decode steps are captured once per batch bucket, largest first, and
+ * replayed; at run time the smallest bucket holding the batch is chosen,
+ * the inputs are copied into the static buffers and the padding rows get
+ * slot -1 (P1, "其余部分": small-model decode is launch-bound, which is what
+ * graphs remove). Each graph holds kv_store and paged_attn_decode (split
+ * pass and merge) on rows [0, bucket) of the buffers below, exactly as the
+ * eager calls would run them; a replay gives the same bits as those calls on
+ * the same buffer contents.
+ *
+ * All buffers are caller-owned device memory that must outlive the handle;
+ * their contents at creation do not matter (creation only captures, it runs
+ * nothing). Before each launch the caller fills rows [0, batch) and makes
+ * the rows up to the chosen bucket padding rows: slot_mapping -1,
+ * context_lens 0 (their output rows are written as zeros). Context lengths
+ * may be anything up to max_context_len. The workspace must be sized by
+ * paged_attn_decode_workspace_size for the largest bucket.
+ */
+typedef struct {
+  const void* key;          /* device bf16 rows [rows, num_kv_heads, head_dim], token stride key_stride elements */
+  int64_t key_stride;
+  const void* value;        /* device bf16, as key */
+  int64_t value_stride;
+  const int32_t* slot_mapping;  /* device int32 [rows] */
+  void* k_cache;            /* device bf16 [num_blocks, block_size, num_kv_heads, head_dim] */
+  void* v_cache;
+  int64_t num_blocks;
+  const void* q;            /* device bf16 [rows, num_q_heads, head_dim] contiguous */
+  void* out;                /* device bf16 [rows, num_q_heads, head_dim] */
+  const int32_t* block_tables;  /* device int32 [rows, block_table_stride] */
+  int32_t block_table_stride;
+  const int32_t* context_lens;  /* device int32 [rows] */
+  void* workspace;          /* device, 256-byte aligned */
+  size_t workspace_bytes;
+  int32_t num_q_heads, num_kv_heads, head_dim, block_size;
+  float scale;
+  int32_t max_context_len;
+} pkv_decode_graph_desc;
+
+typedef struct pkv_decode_graphs pkv_decode_graphs;
+
+/* Capture one graph per bucket (buckets: ascending, >= 1; the largest sets
+ * the number of rows the buffers must hold). Errors of the underlying calls
+ * (shapes, alignment, workspace) are returned as those calls return them;
+ * PKV_ERR_HIP if capture or instantiation fails. The caller owns *out. */
+pkv_status pkv_decode_graphs_create(const pkv_decode_graph_desc* desc, const int32_t* buckets,
+                                    int32_t num_buckets, pkv_decode_graphs** out);
+
+/* Replay the smallest bucket >= batch on `stream`; *out_bucket (if non-NULL)
+ * gets that bucket. PKV_ERR_INVALID if batch is outside [1, largest bucket]. */
+pkv_status pkv_decode_graphs_launch(pkv_decode_graphs* g, int32_t batch, int32_t* out_bucket, void* stream);
+
+pkv_status pkv_decode_graphs_destroy(pkv_decode_graphs* g);
 
 #ifdef __cplusplus
 }

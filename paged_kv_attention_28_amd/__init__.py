@@ -9,6 +9,7 @@ call does, and raises if it is missing (there is no CPU fallback).
 
 from .binding import (  # noqa: F401
     EXPORTS,
+    DecodeGraphs,
     LIB_PATH,
     PkvError,
     SchedStep,

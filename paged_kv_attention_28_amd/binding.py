@@ -22,8 +22,9 @@ STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "HIP", 4: "WORKSPACE"}
 EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_varlen",
            "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
-           "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks")
-ABI_VERSION = 3
+           "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks", "pkv_decode_graphs_create",
+           "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy")
+ABI_VERSION = 4
 
 
 class PkvError(RuntimeError):
@@ -33,6 +34,17 @@ class PkvError(RuntimeError):
 
 
 _lib = None
+
+
+class DecodeGraphDesc(ctypes.Structure):
+    """pkv_decode_graph_desc (include/pkv.h)."""
+    _fields_ = [("key", ctypes.c_void_p), ("key_stride", ctypes.c_int64), ("value", ctypes.c_void_p),
+                ("value_stride", ctypes.c_int64), ("slot_mapping", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("v_cache", ctypes.c_void_p), ("num_blocks", ctypes.c_int64), ("q", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("block_tables", ctypes.c_void_p), ("block_table_stride", ctypes.c_int32),
+                ("context_lens", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("scale", ctypes.c_float), ("max_context_len", ctypes.c_int32)]
 
 
 class SchedBatch(ctypes.Structure):
@@ -93,6 +105,12 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_sched_unfinished.argtypes = [c_vp]
     lib.pkv_sched_free_blocks.restype = c_i32
     lib.pkv_sched_free_blocks.argtypes = [c_vp]
+    lib.pkv_decode_graphs_create.restype = c_i32
+    lib.pkv_decode_graphs_create.argtypes = [ctypes.POINTER(DecodeGraphDesc), P_I32, c_i32, ctypes.POINTER(c_vp)]
+    lib.pkv_decode_graphs_launch.restype = c_i32
+    lib.pkv_decode_graphs_launch.argtypes = [c_vp, c_i32, P_I32, c_vp]
+    lib.pkv_decode_graphs_destroy.restype = c_i32
+    lib.pkv_decode_graphs_destroy.argtypes = [c_vp]
     if lib.pkv_abi_version() != ABI_VERSION:
         raise RuntimeError("libpkv.so ABI version mismatch")
     _lib = lib
@@ -377,3 +395,67 @@ def paged_attn_prefill_varlen(out, q, cu_seqlens_q, context_lens, k_cache, v_cac
                                        T, int(max_q_len), int(max_context_len), Hq, Hkv, D, B, N, float(scale),
                                        wi_ptr, int(wi_n), _stream(stream))
     _check("paged_attn_prefill_varlen", st)
+
+
+class DecodeGraphs:
+    """Decode-step graphs (``pkv_decode_graphs_*``) over static device
+    buffers: key/value [rows, H_kv, D], slot_mapping [rows], q/out
+    [rows, H_q, D], block_tables [rows, stride], context_lens [rows] and a
+    workspace sized for the largest bucket. The tensors are kept alive with
+    the handle; fill rows [0, batch), pad the rest up to the bucket (slot -1,
+    context 0) and call ``launch(batch)``."""
+
+    def __init__(self, key, value, slot_mapping, k_cache, v_cache, q, out, block_tables, context_lens, workspace,
+                 scale, max_context_len, buckets):
+        torch = _torch()
+        self._lib = load_library()
+        self._keep = (key, value, slot_mapping, k_cache, v_cache, q, out, block_tables, context_lens, workspace)
+        N, B, Hkv, D = k_cache.shape
+        d = DecodeGraphDesc()
+        d.key = _dev(key, "key", torch.bfloat16, False)
+        d.key_stride = key.stride(0)
+        d.value = _dev(value, "value", torch.bfloat16, False)
+        d.value_stride = value.stride(0)
+        d.slot_mapping = _dev(slot_mapping, "slot_mapping", torch.int32)
+        d.k_cache = _dev(k_cache, "k_cache", torch.bfloat16)
+        d.v_cache = _dev(v_cache, "v_cache", torch.bfloat16)
+        d.num_blocks = N
+        d.q = _dev(q, "q", torch.bfloat16)
+        d.out = _dev(out, "out", torch.bfloat16)
+        d.block_tables = _dev(block_tables, "block_tables", torch.int32)
+        d.block_table_stride = block_tables.stride(0)
+        d.context_lens = _dev(context_lens, "context_lens", torch.int32)
+        d.workspace = _dev(workspace, "workspace", workspace.dtype)
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+        d.num_q_heads, d.num_kv_heads, d.head_dim, d.block_size = q.shape[1], Hkv, D, B
+        d.scale = float(scale)
+        d.max_context_len = int(max_context_len)
+        rows = max(buckets)
+        for t, nm in ((key, "key"), (value, "value"), (slot_mapping, "slot_mapping"), (q, "q"), (out, "out"),
+                      (block_tables, "block_tables"), (context_lens, "context_lens")):
+            if t.shape[0] < rows:
+                raise ValueError(f"{nm} has {t.shape[0]} rows, the largest bucket needs {rows}")
+        self.buckets = sorted(int(b) for b in buckets)
+        arr = (ctypes.c_int32 * len(self.buckets))(*self.buckets)
+        h = c_vp()
+        _check("pkv_decode_graphs_create", self._lib.pkv_decode_graphs_create(ctypes.byref(d), arr, len(self.buckets),
+                                                                              ctypes.byref(h)))
+        self._h = h
+
+    def launch(self, batch: int, stream=None) -> int:
+        """Replay the smallest bucket >= batch; returns that bucket."""
+        b = ctypes.c_int32(0)
+        _check("pkv_decode_graphs_launch", self._lib.pkv_decode_graphs_launch(self._h, int(batch), ctypes.byref(b),
+                                                                              _stream(stream)))
+        return b.value
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_decode_graphs_destroy(self._h)
+            self._h = c_vp()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

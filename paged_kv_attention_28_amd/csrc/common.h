@@ -15,6 +15,11 @@ constexpr int kBlockSize = 256;  // tokens per cache block
 pkv_status fail(pkv_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 // Returns PKV_OK, or PKV_ERR_HIP with the runtime's message after a launch.
 pkv_status check_launch(const char* what);
+
+// Queries (and caches) the decode kernel's resident work-group count for a
+// call with these head counts and sequence count, so that a later call made
+// under stream capture finds it cached; false if the device cannot be queried.
+bool decode_prepare(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs);
 // Clears the thread's error message (called on every successful entry).
 pkv_status ok();
 

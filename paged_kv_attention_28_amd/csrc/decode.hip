@@ -555,6 +555,11 @@ int resident_wgs(const void* kernel, size_t lds) {
 
 }  // namespace
 
+bool decode_prepare(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs) {
+  if (num_kv_heads < 1 || num_q_heads < num_kv_heads || num_q_heads % num_kv_heads || num_seqs < 1) return false;
+  return resident_wgs(pick_kernel(num_q_heads / num_kv_heads, num_kv_heads), (size_t)(num_seqs + 1) * 4) > 0;
+}
+
 }  // namespace pkv
 
 extern "C" size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

@@ -296,6 +296,66 @@ def test_empty_calls_are_noops():
     assert (dw.k_cache.view(torch.int16) == H.NAN_BF16).all()
 
 
+def test_decode_graphs_replay_matches_eager():
+    """Decode-step graphs (store + decode per bucket) give the bits of the
+    eager calls on the same static buffers, for batches that hit an exact
+    bucket and batches that need padding rows; each graph is replayed three
+    times with unrelated eager work and synchronisation in between, and the
+    real rows are also checked against the oracle."""
+    import paged_kv_attention_28_amd as P
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(1, 1500, size=64)]
+    w = custom(lens, [L - 1 for L in lens], kind="decode", seed=31)
+    dw = H.DeviceWorkload(w).build()
+    kc_ref, vc_ref = O.build_caches(w, device="cuda")
+    p = w.passes[0]
+    q_all, m_all = dw.pass_inputs(p)
+    k_all, v_all = W.store_kv(w, "cuda")
+    buckets = [1, 2, 4, 8, 16, 32, 48, 64]
+    rows, mb = 64, w.max_blocks_per_seq
+    dev = "cuda"
+    key = torch.zeros(rows, 8, 128, dtype=torch.bfloat16, device=dev)
+    value = torch.zeros_like(key)
+    slots = torch.full((rows,), -1, dtype=torch.int32, device=dev)
+    q = torch.zeros(rows, 16, 128, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    bt = torch.full((rows, mb), -1, dtype=torch.int32, device=dev)
+    ctx = torch.zeros(rows, dtype=torch.int32, device=dev)
+    max_ctx = mb * 256
+    ws = torch.empty(P.paged_attn_decode_workspace_size(rows, 16, 8, 128, max_ctx), dtype=torch.uint8, device=dev)
+    graphs = P.DecodeGraphs(key, value, slots, dw.k_cache, dw.v_cache, q, out, bt, ctx, ws, w.scale, max_ctx, buckets)
+    ws_eager = torch.empty_like(ws)
+    junk = torch.randn(512, 512, device=dev)
+    slot_all = dw.store_slots()
+    for batch in (1, 3, 17, 48, 64):
+        bucket = min(b for b in buckets if b >= batch)
+        key.zero_(), value.zero_(), q.zero_(), slots.fill_(-1), bt.fill_(-1), ctx.zero_()
+        key[:batch], value[:batch], q[:batch] = k_all[:batch], v_all[:batch], q_all[:batch]
+        slots[:batch] = slot_all[:batch]
+        bt[:batch] = m_all.block_tables[:batch]
+        ctx[:batch] = m_all.context_lens[:batch]
+        torch.cuda.synchronize()
+        # eager reference on the same buffers and the same bucket of rows
+        P.kv_store(key[:bucket], value[:bucket], dw.k_cache, dw.v_cache, slots[:bucket])
+        ref = torch.empty(bucket, 16, 128, dtype=torch.bfloat16, device=dev)
+        P.paged_attn_decode(ref, q[:bucket], dw.k_cache, dw.v_cache, bt[:bucket], ctx[:bucket], w.scale, max_ctx,
+                            ws_eager)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            out.fill_(7.0)
+            assert graphs.launch(batch) == bucket
+            torch.cuda.synchronize()
+            assert torch.equal(out[:bucket].view(torch.int16), ref.view(torch.int16)), (batch, rep)
+            assert (out[batch:bucket].float() == 0).all()
+            (junk @ junk).sum().item()   # unrelated eager work between replays
+        assert np.array_equal(_cache_bits(dw.k_cache), kc_ref)
+        oracle = O.run_pass(w, p, kc_ref, vc_ref, q=q_all)
+        assert_close(out[:batch], oracle[:batch], None, f"graph batch {batch}")
+    with pytest.raises(P.PkvError):
+        graphs.launch(65)
+    graphs.close()
+
+
 # ----------------------------------------------------------------------------
 # configuration 5: scheduler-trace replay over 28 layers
 # ----------------------------------------------------------------------------
