@@ -165,6 +165,65 @@ def time_steps(runner, steps: int, warmup: int, torch):
     return wall / steps * 1e3, store_ms, attn_ms
 
 
+def graph_vs_eager(torch, dev, iters: int = 200):
+    """Host-side cost of a decode step (store + attention) issued eagerly
+    through the binding versus replayed from a captured graph, on decode
+    batches shaped like the scheduler replay's (contexts U[100, 1024]),
+    where launch overhead matters most."""
+    from paged_kv_attention_28_amd import binding as B
+    rng = np.random.default_rng(7)
+    rows, mb, hq, hkv, d = 256, 4, 16, 8, 128
+    lens = rng.integers(100, 1025, size=rows).astype(np.int32)
+    nblk = rows * mb
+    kc = torch.randn(nblk, 256, hkv, d, device=dev).to(torch.bfloat16)
+    vc = torch.randn_like(kc)
+    bt_h = np.arange(nblk, dtype=np.int32).reshape(rows, mb)
+    pos = lens - 1
+    slots_h = (bt_h[np.arange(rows), pos // 256] * 256 + pos % 256).astype(np.int32)
+    bt = torch.from_numpy(bt_h).to(dev)
+    ctx = torch.from_numpy(lens).to(dev)
+    slots = torch.from_numpy(slots_h).to(dev)
+    key = torch.randn(rows, hkv, d, device=dev).to(torch.bfloat16)
+    value = torch.randn_like(key)
+    q = torch.randn(rows, hq, d, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    max_ctx = mb * 256
+    ws = torch.empty(B.paged_attn_decode_workspace_size(rows, hq, hkv, d, max_ctx), dtype=torch.uint8, device=dev)
+    buckets = [1, 2, 4, 8] + list(range(16, rows + 1, 16))
+    graphs = B.DecodeGraphs(key, value, slots, kc, vc, q, out, bt, ctx, ws, 1.0 / np.sqrt(d), max_ctx, buckets)
+    scale = 1.0 / float(np.sqrt(d))
+    res = []
+    for batch in (1, 16, 64, 256):
+        views = (key[:batch], value[:batch], slots[:batch], q[:batch], out[:batch], bt[:batch], ctx[:batch])
+
+        def eager():
+            B.kv_store(views[0], views[1], kc, vc, views[2])
+            B.paged_attn_decode(views[4], views[3], kc, vc, views[5], views[6], scale, max_ctx, ws)
+
+        for f in (eager, lambda: graphs.launch(batch)):
+            for _ in range(10):
+                f()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            eager()
+        torch.cuda.synchronize()
+        t_e = (time.perf_counter() - t0) / iters * 1e6
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            graphs.launch(batch)
+        torch.cuda.synchronize()
+        t_g = (time.perf_counter() - t0) / iters * 1e6
+        res.append({"batch": batch, "bucket": min(b for b in buckets if b >= batch), "eager_us": round(t_e, 2),
+                    "graph_us": round(t_g, 2)})
+        log(f"[bench] decode step batch {batch}: eager {t_e:.1f} us, graph {t_g:.1f} us")
+    graphs.close()
+    return {"workload": "decode steps (kv_store + paged_attn_decode) of 1/16/64/256 sequences, contexts U[100,1024], "
+                        "16Q/8KV, d128; wall-clock per step over back-to-back steps, eager calls through the binding "
+                        "vs graph replay of the smallest bucket",
+            "batches": res}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +231,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; multi-GPU runs are not supported (got --gpus {args.gpus})",
@@ -230,6 +290,8 @@ def main():
                    "store_us": round(float(pstore.mean()) * 1e3, 2), "store_gbs": round(store_gbs, 1),
                    "flops": pw["flops"], "pairs": pw["pairs"]}
 
+    graph = None if args.no_graph else graph_vs_eager(torch, dev)
+
     line = {
         "metric": "decode attn GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak",
         "value": round(value, 2),
@@ -255,6 +317,7 @@ def main():
                      "algorithmic_bytes": db["attn"], "us": round(attn_avg * 1e3, 2)},
         "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
         "prefill": prefill,
+        "decode_graph": graph,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
