@@ -59,7 +59,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -369,6 +369,45 @@ pkv_status pkv_decode_graphs_create(const pkv_decode_graph_desc* desc, const int
 pkv_status pkv_decode_graphs_launch(pkv_decode_graphs* g, int32_t batch, int32_t* out_bucket, void* stream);
 
 pkv_status pkv_decode_graphs_destroy(pkv_decode_graphs* g);
+
+/*
+ * rope_kv_store — rotary position embedding of q and k fused with kv_store.
+ *
+ * P2, attention-layer sketch: q and k are rotated by their positions, then
+ * K and V are written to the cache blocks (P1, "第六站：注意力层": row `slot`
+ * of the cache, slot -1 skipped). The pages give no rotation formula; this
+ * library uses the "rotate half" form: element i of a head (i < head_dim/2)
+ * pairs with element i + head_dim/2 and the pair turns by the angle whose
+ * cosine and sine are cos_sin[pos][i] and cos_sin[pos][head_dim/2 + i]
+ * (pkv_rope_cos_sin builds that table for pos * theta^(-2i/head_dim)).
+ * Arithmetic in fp32, results rounded to bf16 (nearest even).
+ *
+ *   q            device bf16 [num_tokens, num_q_heads, head_dim] with token
+ *                stride q_stride elements; rotated in place (every row,
+ *                padding rows included)
+ *   key, value   device bf16 [num_tokens, num_kv_heads, head_dim] rows with
+ *                token strides key_stride / value_stride elements (read only)
+ *   positions    device int32 [num_tokens], 0 <= pos < max_position
+ *                (values outside are clamped into the table)
+ *   cos_sin      device float [max_position, head_dim]
+ *   slot_mapping device int32 [num_tokens]: rotated K and V of token t go to
+ *                row slot_mapping[t] of the caches; -1 (or any slot outside
+ *                the pool) stores nothing
+ * head_dim 128, block_size 256, num_kv_heads in {1, 2, 4, 8}, num_q_heads
+ * 1..64; q, key, value, caches and table 16-byte aligned; strides multiples
+ * of 8 elements. Slots must be distinct within one call.
+ */
+pkv_status rope_kv_store(void* q, int64_t q_stride, const void* key, int64_t key_stride, const void* value,
+                         int64_t value_stride, const int32_t* positions, const float* cos_sin,
+                         int32_t max_position, void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                         int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int64_t num_blocks, void* stream);
+
+/* Host: out[pos][i] = cos(pos * theta^(-2i/head_dim)), out[pos][head_dim/2 + i]
+ * = the sine, for pos < max_position, i < head_dim/2; computed in double and
+ * rounded to float. out is host float [max_position, head_dim]; head_dim
+ * even, theta > 1. */
+pkv_status pkv_rope_cos_sin(float* out, int32_t max_position, int32_t head_dim, double theta);
 
 #ifdef __cplusplus
 }

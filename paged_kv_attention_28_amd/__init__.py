@@ -23,5 +23,7 @@ from .binding import (  # noqa: F401
     paged_attn_prefill_varlen,
     pkv_prefill_plan,
     pkv_prepare_step,
+    pkv_rope_cos_sin,
+    rope_kv_store,
     prefill_plan_capacity,
 )

@@ -23,8 +23,8 @@ EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_varlen",
            "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
            "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks", "pkv_decode_graphs_create",
-           "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy")
-ABI_VERSION = 4
+           "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy", "rope_kv_store", "pkv_rope_cos_sin")
+ABI_VERSION = 5
 
 
 class PkvError(RuntimeError):
@@ -111,6 +111,11 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_decode_graphs_launch.argtypes = [c_vp, c_i32, P_I32, c_vp]
     lib.pkv_decode_graphs_destroy.restype = c_i32
     lib.pkv_decode_graphs_destroy.argtypes = [c_vp]
+    lib.rope_kv_store.restype = c_i32
+    lib.rope_kv_store.argtypes = [c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i64,
+                                  c_i32, c_i32, c_i32, c_i32, c_i64, c_vp]
+    lib.pkv_rope_cos_sin.restype = c_i32
+    lib.pkv_rope_cos_sin.argtypes = [ctypes.POINTER(ctypes.c_float), c_i32, c_i32, ctypes.c_double]
     if lib.pkv_abi_version() != ABI_VERSION:
         raise RuntimeError("libpkv.so ABI version mismatch")
     _lib = lib
@@ -337,6 +342,38 @@ def kv_store(key, value, k_cache, v_cache, slot_mapping, stream=None):
                       _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
                       _dev(slot_mapping, "slot_mapping", torch.int32), T, H, D, B, N, _stream(stream))
     _check("kv_store", st)
+
+
+def pkv_rope_cos_sin(max_position: int, head_dim: int = 128, theta: float = 1.0e6) -> np.ndarray:
+    """Host float32 [max_position, head_dim] table: cos of each pair's angle,
+    then its sine (``pkv_rope_cos_sin``)."""
+    lib = load_library()
+    out = np.empty((int(max_position), int(head_dim)), dtype=np.float32)
+    _check("pkv_rope_cos_sin", lib.pkv_rope_cos_sin(out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                                     int(max_position), int(head_dim), float(theta)))
+    return out
+
+
+def rope_kv_store(q, key, value, positions, cos_sin, k_cache, v_cache, slot_mapping, stream=None):
+    """q [T, H_q, D] bf16 (rotated in place; token stride may exceed a row);
+    key/value [T, H_kv, D] bf16; positions, slot_mapping [T] int32; cos_sin
+    [max_position, D] float32 device table; caches [N, 256, H_kv, 128]."""
+    torch = _torch()
+    lib = load_library()
+    T = q.shape[0]
+    if key.shape[0] != T or value.shape[0] != T or slot_mapping.shape[0] != T or positions.shape[0] != T:
+        raise ValueError("q, key, value, positions and slot_mapping must have the same number of tokens")
+    for t, n in ((q, "q"), (key, "key"), (value, "value")):
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{n} rows must be contiguous [H, D]")
+    N, B, H, D = k_cache.shape
+    st = lib.rope_kv_store(_dev(q, "q", torch.bfloat16, False), q.stride(0), _dev(key, "key", torch.bfloat16, False),
+                           key.stride(0), _dev(value, "value", torch.bfloat16, False), value.stride(0),
+                           _dev(positions, "positions", torch.int32), _dev(cos_sin, "cos_sin", torch.float32),
+                           cos_sin.shape[0], _dev(k_cache, "k_cache", torch.bfloat16),
+                           _dev(v_cache, "v_cache", torch.bfloat16), _dev(slot_mapping, "slot_mapping", torch.int32),
+                           T, q.shape[1], H, D, B, N, _stream(stream))
+    _check("rope_kv_store", st)
 
 
 def paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:

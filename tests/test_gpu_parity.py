@@ -356,6 +356,69 @@ def test_decode_graphs_replay_matches_eager():
     graphs.close()
 
 
+def _within_one_bf16_unit(gpu, ref, what):
+    """|gpu - ref| within one bf16 unit of the exact value (1e-5 floor for
+    results near zero, where the fp32 products' own rounding dominates)."""
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-30)))
+    tol = np.maximum(2.0 ** (e - 7), 1e-5)
+    bad = np.abs(gpu - ref) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond one bf16 unit, worst {np.abs(gpu - ref).max():.3e}"
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 2)])
+def test_rope_kv_store_parity(hq, hkv):
+    """Fused rotary + store against the oracle: rotated q (every row) and the
+    stored rotated K rows within one bf16 unit of the fp64 rotation; V rows
+    and every row not written bit-exact (slot -1 rows and positions from
+    0 to 40959 included)."""
+    import paged_kv_attention_28_amd as P
+    from oracle import rope as orope
+    rng = np.random.default_rng(41)
+    lens = [1, 300, 1000, 5000, 40960]
+    cached = [0, 17, 999, 4000, 40900]
+    nb = [-(-L // 256) for L in lens]
+    num_blocks = sum(nb) + 3
+    perm = rng.permutation(num_blocks)
+    tables, o = [], 0
+    for n in nb:
+        tables.append([int(b) for b in perm[o:o + n]])
+        o += n
+    m = P.pkv_prepare_step(lens, cached, tables, 256, max(nb), num_pad=5)
+    T = m.num_tokens
+    pos = np.concatenate([np.arange(c, L) for c, L in zip(cached, lens)] + [np.zeros(5, dtype=np.int64)]).astype(np.int32)
+    assert pos.size == T
+    q = W.randn_bf16(41, 1, W.TAG_Q, (T, hq, 128), "cuda")
+    k = W.randn_bf16(41, 1, W.TAG_K, (T, hkv, 128), "cuda")
+    v = W.randn_bf16(41, 1, W.TAG_V, (T, hkv, 128), "cuda")
+    tab = torch.from_numpy(P.pkv_rope_cos_sin(40960, 128, 1.0e6)).cuda()
+    kc = torch.empty(num_blocks, 256, hkv, 128, dtype=torch.bfloat16, device="cuda")
+    kc.view(torch.int16).fill_(H.NAN_BF16)
+    vc = torch.empty_like(kc)
+    vc.view(torch.int16).fill_(H.NAN_BF16)
+    qg = q.clone()
+    slots = torch.from_numpy(np.ascontiguousarray(m.slot_mapping)).cuda()
+    P.rope_kv_store(qg, k, v, torch.from_numpy(pos).cuda(), tab, kc, vc, slots)
+    torch.cuda.synchronize()
+    kc0 = np.full((num_blocks, 256, hkv, 128), H.NAN_BF16, dtype=np.uint16)
+    q_rot, k_rot, kc_ref, vc_ref = orope.rope_kv_store_ref(O.bits(q), O.bits(k), O.bits(v), pos, m.slot_mapping,
+                                                           kc0, kc0.copy())
+    _within_one_bf16_unit(_f64(qg), q_rot, "q")
+    got_k, got_v = _cache_bits(kc), _cache_bits(vc)
+    assert np.array_equal(got_v, vc_ref)
+    live = m.slot_mapping >= 0
+    rows = m.slot_mapping[live]
+    flat = got_k.reshape(-1, hkv, 128)
+    _within_one_bf16_unit(op_bits_to_f64(flat[rows]), k_rot[live], "k")
+    others = np.ones(flat.shape[0], dtype=bool)
+    others[rows] = False
+    assert (flat[others] == H.NAN_BF16).all()
+
+
+def op_bits_to_f64(bits):
+    from oracle import paged as op
+    return op.bf16_bits_to_f64(bits)
+
+
 # ----------------------------------------------------------------------------
 # configuration 5: scheduler-trace replay over 28 layers
 # ----------------------------------------------------------------------------
