@@ -165,6 +165,65 @@ def time_steps(runner, steps: int, warmup: int, torch):
     return wall / steps * 1e3, store_ms, attn_ms
 
 
+def rope_store_rate(torch, w, runner, reps: int):
+    """rope_kv_store on the prefill step's tokens (positions num_cached ..
+    len - 1 of each sequence): HIP events around each call on its stream.
+    Algorithmic bytes per token: q read and written, K and V read, rotated K
+    and V written, one cos/sin table row."""
+    from paged_kv_attention_28_amd import binding as B
+    b = w.passes[0].batch
+    pos = np.concatenate([np.arange(s.num_cached, s.seq_len) for s in b.seqs]).astype(np.int32)
+    max_pos = int(max(s.seq_len for s in b.seqs))
+    tab = torch.from_numpy(B.pkv_rope_cos_sin(max_pos, w.head_dim)).to(runner.q.device)
+    posd = torch.from_numpy(pos).to(runner.q.device)
+    q = runner.q.clone()
+    slots = runner.dev_meta[0]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for _ in range(3):
+        B.rope_kv_store(q, runner.k, runner.v, posd, tab, runner.dw.k_cache, runner.dw.v_cache, slots)
+    for e in ev:
+        e[0].record()
+        B.rope_kv_store(q, runner.k, runner.v, posd, tab, runner.dw.k_cache, runner.dw.v_cache, slots)
+        e[1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    per_tok = 2 * w.num_q_heads * w.head_dim * 2 + 4 * w.num_kv_heads * w.head_dim * 2 + w.head_dim * 4
+    nbytes = pos.size * per_tok
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"[bench] rope_kv_store on {pos.size} prefill tokens: {us:.1f} us -> {gbs:.0f} GB/s "
+        f"({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+    return {"tokens": int(pos.size), "us": round(us, 2), "gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "bytes_per_token": per_tok}
+
+
+def sampler_rate(torch, dev, reps: int = 20):
+    """sample_temperature on a 256-row decode batch over a 151936-entry
+    vocabulary (fp32 logits and Gumbel noise): HIP events per call.
+    Algorithmic bytes: logit + noise per entry."""
+    from paged_kv_attention_28_amd import binding as B
+    rows, vocab = 256, 151936
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    logits = torch.randn(rows, vocab, device=dev, generator=g)
+    noise = -torch.log(torch.empty(rows, vocab, device=dev).exponential_(generator=g))
+    temps = torch.full((rows,), 0.7, device=dev)
+    out = torch.empty(rows, dtype=torch.int32, device=dev)
+    ws = torch.empty(B.sample_temperature_workspace_size(rows, vocab), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        B.sample_temperature(out, logits, temps, noise, ws)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        B.sample_temperature(out, logits, temps, noise, ws)
+        e[1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    gbs = rows * vocab * 8 / (us * 1e-6) / 1e9
+    log(f"[bench] sample_temperature {rows} x {vocab}: {us:.1f} us -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%})")
+    return {"rows": rows, "vocab": vocab, "us": round(us, 2), "gbs": round(gbs, 1),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
+
+
 def graph_vs_eager(torch, dev, iters: int = 200):
     """Host-side cost of a decode step (store + attention) issued eagerly
     through the binding versus replayed from a captured graph, on decode
@@ -282,15 +341,17 @@ def main():
         log(f"[bench] prefill step {pms * 1e3:.1f} us wall; store {pstore.mean() * 1e3:.1f} us "
             f"({store_gbs:.0f} GB/s), attention {pav * 1e3:.1f} us -> {tflops:.1f} TFLOP/s "
             f"({tflops / BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+        rope = rope_store_rate(torch, wp, rp, max(args.steps // 2, 5))
         prefill = {"workload": "chunked prefill: 36 seqs, 16124 new tokens (budget 16384), prompts U[100,1024], "
                                "about half with a shared 256/512-token cached prefix, first seq a mid-block chunk "
                                "continuation; 16Q/8KV, d128, bf16, block 256",
                    "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
                    "attn_us": round(pav * 1e3, 2), "step_us_wall": round(pms * 1e3, 2),
                    "store_us": round(float(pstore.mean()) * 1e3, 2), "store_gbs": round(store_gbs, 1),
-                   "flops": pw["flops"], "pairs": pw["pairs"]}
+                   "flops": pw["flops"], "pairs": pw["pairs"], "rope_kv_store": rope}
 
     graph = None if args.no_graph else graph_vs_eager(torch, dev)
+    sampler = sampler_rate(torch, dev)
 
     line = {
         "metric": "decode attn GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak",
@@ -318,6 +379,7 @@ def main():
         "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
         "prefill": prefill,
         "decode_graph": graph,
+        "sampler": sampler,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -59,7 +59,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -408,6 +408,32 @@ pkv_status rope_kv_store(void* q, int64_t q_stride, const void* key, int64_t key
  * rounded to float. out is host float [max_position, head_dim]; head_dim
  * even, theta > 1. */
 pkv_status pkv_rope_cos_sin(float* out, int32_t max_position, int32_t head_dim, double theta);
+
+/*
+ * sample_temperature — one token per row (P1, "它省略了什么" and "第一站：主循环":
+ * temperature only, the argmax of the probabilities divided by Exp(1) noise,
+ * a draw with the multinomial's distribution; temperature 0 not allowed).
+ * With g = -ln E supplied by the caller, the token is the first index j of
+ * the largest key fp32(fp32(logits[j] * fp32(1 / T)) + g[j]) (the log of
+ * the softmax differs from logits / T by a per-row constant); every step is
+ * one correctly rounded fp32 operation, so the choice can be reproduced
+ * exactly off the device.
+ *
+ *   out_tokens    device int32 [num_rows] (written)
+ *   logits        device float [num_rows, vocab], row stride logits_stride
+ *   temperatures  device float [num_rows], finite and > 0 (caller contract)
+ *   gumbel        device float [num_rows, vocab], row stride gumbel_stride:
+ *                 -ln E for independent Exp(1) draws E (finite)
+ *   workspace     device, 16-byte aligned, sample_temperature_workspace_size
+ *                 bytes; no initialisation needed
+ * logits and gumbel 16-byte aligned with strides multiples of 4 elements.
+ * Deterministic (no atomics).
+ */
+size_t sample_temperature_workspace_size(int32_t num_rows, int32_t vocab);
+pkv_status sample_temperature(int32_t* out_tokens, const float* logits, int64_t logits_stride,
+                              const float* temperatures, const float* gumbel, int64_t gumbel_stride,
+                              int32_t num_rows, int32_t vocab, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 #ifdef __cplusplus
 }

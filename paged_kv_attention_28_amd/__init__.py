@@ -25,5 +25,7 @@ from .binding import (  # noqa: F401
     pkv_prepare_step,
     pkv_rope_cos_sin,
     rope_kv_store,
+    sample_temperature,
+    sample_temperature_workspace_size,
     prefill_plan_capacity,
 )

@@ -23,8 +23,9 @@ EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_varlen",
            "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
            "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks", "pkv_decode_graphs_create",
-           "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy", "rope_kv_store", "pkv_rope_cos_sin")
-ABI_VERSION = 5
+           "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy", "rope_kv_store", "pkv_rope_cos_sin",
+           "sample_temperature_workspace_size", "sample_temperature")
+ABI_VERSION = 6
 
 
 class PkvError(RuntimeError):
@@ -114,6 +115,10 @@ def load_library(path: str = LIB_PATH):
     lib.rope_kv_store.restype = c_i32
     lib.rope_kv_store.argtypes = [c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_vp, c_vp, c_i64,
                                   c_i32, c_i32, c_i32, c_i32, c_i64, c_vp]
+    lib.sample_temperature_workspace_size.restype = c_size
+    lib.sample_temperature_workspace_size.argtypes = [c_i32, c_i32]
+    lib.sample_temperature.restype = c_i32
+    lib.sample_temperature.argtypes = [c_vp, c_vp, c_i64, c_vp, c_vp, c_i64, c_i32, c_i32, c_vp, c_size, c_vp]
     lib.pkv_rope_cos_sin.restype = c_i32
     lib.pkv_rope_cos_sin.argtypes = [ctypes.POINTER(ctypes.c_float), c_i32, c_i32, ctypes.c_double]
     if lib.pkv_abi_version() != ABI_VERSION:
@@ -374,6 +379,32 @@ def rope_kv_store(q, key, value, positions, cos_sin, k_cache, v_cache, slot_mapp
                            _dev(v_cache, "v_cache", torch.bfloat16), _dev(slot_mapping, "slot_mapping", torch.int32),
                            T, q.shape[1], H, D, B, N, _stream(stream))
     _check("rope_kv_store", st)
+
+
+def sample_temperature_workspace_size(num_rows: int, vocab: int) -> int:
+    return int(load_library().sample_temperature_workspace_size(int(num_rows), int(vocab)))
+
+
+def sample_temperature(out_tokens, logits, temperatures, gumbel, workspace=None, stream=None):
+    """out_tokens [R] int32; logits, gumbel [R, V] float32 (row stride may
+    exceed V); temperatures [R] float32; workspace uint8 (allocated if None)."""
+    torch = _torch()
+    lib = load_library()
+    R, V = logits.shape
+    if gumbel.shape != logits.shape or temperatures.shape[0] != R or out_tokens.shape[0] != R:
+        raise ValueError("shapes of logits, gumbel, temperatures and out_tokens do not match")
+    for t, n in ((logits, "logits"), (gumbel, "gumbel")):
+        if t.stride(1) != 1:
+            raise ValueError(f"{n} rows must be contiguous")
+    if workspace is None:
+        workspace = torch.empty(max(sample_temperature_workspace_size(R, V), 16), dtype=torch.uint8,
+                                device=logits.device)
+    st = lib.sample_temperature(_dev(out_tokens, "out_tokens", torch.int32), _dev(logits, "logits", torch.float32, False),
+                                logits.stride(0), _dev(temperatures, "temperatures", torch.float32),
+                                _dev(gumbel, "gumbel", torch.float32, False), gumbel.stride(0), R, V,
+                                _dev(workspace, "workspace", workspace.dtype),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("sample_temperature", st)
 
 
 def paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len) -> int:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["api.cpp", "sched.cpp", "graph.cpp", "kv_store.hip", "rope_store.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "sched.cpp", "graph.cpp", "kv_store.hip", "rope_store.hip", "sampler.hip", "decode.hip", "prefill.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 

@@ -419,6 +419,29 @@ def op_bits_to_f64(bits):
     return op.bf16_bits_to_f64(bits)
 
 
+@pytest.mark.parametrize("rows,vocab,pad", [(37, 151936, 0), (256, 151936, 64), (3, 1001, 3), (1, 4, 0)])
+def test_sampler_matches_oracle_decision(rows, vocab, pad):
+    """Token ids equal the oracle's fp32 decision exactly (ties included:
+    some rows repeat their maximum logit with zero noise there)."""
+    import paged_kv_attention_28_amd as P
+    from oracle import sampler as OSm
+    rng = np.random.default_rng(rows * 7 + vocab)
+    logits = (rng.standard_normal((rows, vocab + pad)) * 4).astype(np.float32)
+    g = (-np.log(rng.exponential(size=(rows, vocab + pad)))).astype(np.float32)
+    for r in range(0, rows, 5):            # ties: the top logit repeated, no noise on those entries
+        j = np.argsort(-logits[r, :vocab])[:3]
+        logits[r, j] = logits[r, j[0]]
+        g[r, j] = 0.0
+        g[r, :vocab] = np.minimum(g[r, :vocab], 0.0)
+    temps = rng.uniform(0.2, 2.0, size=rows).astype(np.float32)
+    dl = torch.from_numpy(logits).cuda()[:, :vocab]
+    dg = torch.from_numpy(g).cuda()[:, :vocab]
+    out = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
+    P.sample_temperature(out, dl, torch.from_numpy(temps).cuda(), dg)
+    want = OSm.sample_decision(logits[:, :vocab], temps, g[:, :vocab])
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
 # ----------------------------------------------------------------------------
 # configuration 5: scheduler-trace replay over 28 layers
 # ----------------------------------------------------------------------------
