@@ -31,7 +31,8 @@
 //    slot 1 (piece ends it) of that wavefront. The merge kernel (one
 //    work-group per sequence, all heads at once) finds the pieces from the
 //    same step arithmetic and combines them (log-sum-exp in the log2
-//    domain); it also writes zeros for padding rows (context 0). (Merging
+//    domain), loading them 8 at a time with the next 8 already in flight;
+//    it also writes zeros for padding rows (context 0). (Merging
 //    inside the stream kernel would need a device-scope release per piece,
 //    which writes back the whole L2 of the XCD on this GPU.)
 //  * Positions past the context end load the last context row (always
@@ -227,37 +228,52 @@ __global__ __launch_bounds__(HQ * 16) void decode_merge_kernel(uint16_t* __restr
   if (npieces == 1) return;
   float M = kNegBig, lsum = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i0 = 0; i0 < npieces; i0 += 4) {
-    float m[4], l[4];
-    f32x4 lo[4], hi[4];
+  // pieces in batches of 8; the next batch is loaded before the current one
+  // is combined, so only the first batch's latency is exposed
+  constexpr int kBatch = HQ >= 64 ? 4 : 8;  // 1024-thread groups have half the registers
+  struct Piece {
+    float m[kBatch], l[kBatch];
+    f32x4 lo[kBatch], hi[kBatch];
+  };
+  auto load = [&](Piece& pc, int i0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       const int i = i0 + k < npieces ? i0 + k : npieces - 1;
       const int w = wf + i;
       const int slot = (i == 0 && pb != w * P) ? 1 : 0;
       const int64_t pidx = ((int64_t)w * 2 + slot) * HQ + h;
-      m[k] = part_ml[pidx * 2];
-      l[k] = part_ml[pidx * 2 + 1];
-      lo[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0);
-      hi[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0 + 4);
+      pc.m[k] = part_ml[pidx * 2];
+      pc.l[k] = part_ml[pidx * 2 + 1];
+      pc.lo[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0);
+      pc.hi[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0 + 4);
     }
+  };
+  auto combine = [&](const Piece& pc, int i0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < kBatch; ++k) {
       if (i0 + k >= npieces) break;
-      const float mn = fmaxf(M, m[k]);
+      const float mn = fmaxf(M, pc.m[k]);
       const float fa = __builtin_amdgcn_exp2f(M - mn);
-      const float fb = __builtin_amdgcn_exp2f(m[k] - mn);
-      lsum = lsum * fa + l[k] * fb;
-      acc[0] = acc[0] * fa + lo[k].x * fb;
-      acc[1] = acc[1] * fa + lo[k].y * fb;
-      acc[2] = acc[2] * fa + lo[k].z * fb;
-      acc[3] = acc[3] * fa + lo[k].w * fb;
-      acc[4] = acc[4] * fa + hi[k].x * fb;
-      acc[5] = acc[5] * fa + hi[k].y * fb;
-      acc[6] = acc[6] * fa + hi[k].z * fb;
-      acc[7] = acc[7] * fa + hi[k].w * fb;
+      const float fb = __builtin_amdgcn_exp2f(pc.m[k] - mn);
+      lsum = lsum * fa + pc.l[k] * fb;
+      acc[0] = acc[0] * fa + pc.lo[k].x * fb;
+      acc[1] = acc[1] * fa + pc.lo[k].y * fb;
+      acc[2] = acc[2] * fa + pc.lo[k].z * fb;
+      acc[3] = acc[3] * fa + pc.lo[k].w * fb;
+      acc[4] = acc[4] * fa + pc.hi[k].x * fb;
+      acc[5] = acc[5] * fa + pc.hi[k].y * fb;
+      acc[6] = acc[6] * fa + pc.hi[k].z * fb;
+      acc[7] = acc[7] * fa + pc.hi[k].w * fb;
       M = mn;
     }
+  };
+  Piece cur, nxt;
+  load(cur, 0);
+  for (int i0 = 0; i0 < npieces; i0 += kBatch) {
+    const bool more = i0 + kBatch < npieces;
+    if (more) load(nxt, i0 + kBatch);
+    combine(cur, i0);
+    if (more) cur = nxt;
   }
   const float inv = 1.f / lsum;
   *op = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
