@@ -31,9 +31,14 @@
 //  * fp32 online softmax in the log2 domain with lazy rescaling (the
 //    reference max moves only when a row max exceeds it by 8, so most tiles
 //    skip rescaling the 64 output accumulators); fully masked 32-key subtiles
-//    above the causal diagonal are skipped; K/V of tile i+1 are fetched from
-//    HBM into registers while tile i is computed; two LDS buffers, one
-//    barrier per tile.
+//    above the causal diagonal are skipped.
+//  * K/V of tile i+1 go from the cache straight into LDS
+//    (global_load_lds_dwordx4) while tile i is computed: no registers, no
+//    LDS writes by the wavefronts; two LDS buffers, one wait and one barrier
+//    per tile. Such a load writes lane l's 16 bytes at LDS base + 16 l, so
+//    rows cannot be padded; instead the 16-byte chunks of each 256-byte row
+//    are XOR-swizzled (by r % 16 in K, by 4 r % 16 in V), which keeps the
+//    16-byte K reads and the transposing V reads free of bank conflicts.
 //  * Keys past the context end are clamped to the last context row (a valid,
 //    written row) and masked, so stale cache rows never enter the result.
 
@@ -44,11 +49,8 @@ namespace pkv {
 namespace {
 
 constexpr int kKeysPerTile = 64;
-constexpr int kKPitch = kHeadDim + 8;   // K tile row: 272 B; 16-byte reads of 16 rows hit 64 distinct banks
-constexpr int kVPitch = kHeadDim + 32;  // V tile row: 320 B; transposing 8-byte reads of 2x4 rows hit distinct banks
-constexpr int kKTileElems = kKeysPerTile * kKPitch;
-constexpr int kVTileElems = kKeysPerTile * kVPitch;
-constexpr int kBufElems = kKTileElems + kVTileElems;
+constexpr int kRowBytes = kHeadDim * 2;               // one head of one key: 256 B
+constexpr int kTileBytes = kKeysPerTile * kRowBytes;   // a K (or V) tile: 16 KiB, rows unpadded
 constexpr float kNegBig = -1e30f;
 constexpr float kRescaleSlack = 8.f;  // log2 units: the reference max moves only when a row max exceeds it by this
 
@@ -72,51 +74,49 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-struct TileRegs {
-  u32x4 k[4];
-  u32x4 v[4];
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-// K and V of keys [key0, key0 + 64) into registers; both caches share the
-// layout, so one set of offsets serves both. Thread t moves 16-byte chunk
-// (t & 15) of keys (t >> 4) + 16 i; keys past the context end are clamped
-// to its last row.
-__device__ __forceinline__ void fetch_tile(TileRegs& r, const char* __restrict__ kc, const char* __restrict__ vc,
-                                           const int32_t* __restrict__ bt, int key0, int L, int64_t row_bytes,
-                                           int64_t block_bytes, int64_t thread_off, int64_t num_blocks) {
-  int64_t blk = bt[key0 >> 8];
+// K and V of keys [key0, key0 + 64) straight from the cache into LDS
+// (global_load_lds_dwordx4: lane l of an instruction writes its 16 bytes at
+// LDS base + 16 l, whatever address it loads). Wavefront w moves rows
+// 16 w .. 16 w + 15, four rows per instruction. Rows are stored unpadded,
+// with their 16-byte chunks XOR-swizzled so that the operand reads hit
+// distinct banks: physical chunk p of row r holds logical chunk p ^ (r % 16)
+// in K and p ^ (4 r % 16) in V. Keys past the context end load its last row.
+__device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* __restrict__ kc,
+                                           const char* __restrict__ vc, int64_t blk, int key0, int L,
+                                           int64_t row_bytes, int64_t block_bytes, int head_off,
+                                           int64_t num_blocks, const uint32_t (&koff)[4], const uint32_t (&voff)[4]) {
   if (blk < 0 || blk >= num_blocks) blk = 0;  // caller error: stay inside the pool
-  const int64_t base = blk * block_bytes + (int64_t)(key0 & (kBlockSize - 1)) * row_bytes + thread_off;
-  const int local = threadIdx.x >> 4;
+  const int wave = threadIdx.x >> 6;
+  // wave-uniform start of the tile in both caches; lanes add 32-bit offsets
+  const int64_t base = blk * block_bytes + (int64_t)(key0 & (kBlockSize - 1)) * row_bytes + head_off;
+  const char* kb = kc + base;
+  const char* vb = vc + base;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
   if (key0 + kKeysPerTile <= L) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      r.k[i] = *reinterpret_cast<const u32x4*>(kc + base + 16 * i * row_bytes);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vc + base + 16 * i * row_bytes);
+      const int r0 = 16 * wave + 4 * i;
+      __builtin_amdgcn_global_load_lds(kb + koff[i], (lds_void*)(kbuf + r0 * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + voff[i], (lds_void*)(vbuf + r0 * kRowBytes), 16, 0, 0);
     }
   } else {
+    const int lane = threadIdx.x & 63;
+    const int sub = lane >> 4;
     const int last = L - 1 - key0;  // >= 0: the tile starts inside the context
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int kl = local + 16 * i;
-      const int64_t off = base + (int64_t)((kl < last ? kl : last) - local) * row_bytes;
-      r.k[i] = *reinterpret_cast<const u32x4*>(kc + off);
-      r.v[i] = *reinterpret_cast<const u32x4*>(vc + off);
+      const int r0 = 16 * wave + 4 * i;
+      const int r = r0 + sub;
+      const int back = r > last ? r - last : 0;  // rows to step back to the last context row
+      const uint32_t d = (uint32_t)back * (uint32_t)row_bytes;
+      __builtin_amdgcn_global_load_lds(kb + (koff[i] - d), (lds_void*)(kbuf + r0 * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + (voff[i] - d), (lds_void*)(vbuf + r0 * kRowBytes), 16, 0, 0);
     }
   }
-}
-
-__device__ __forceinline__ void stage_tile(const TileRegs& r, uint16_t* buf) {
-  const int t = threadIdx.x;
-  const int part = t & 15;
-  const int local = t >> 4;
-  uint16_t* kt = buf;
-  uint16_t* vt = buf + kKTileElems;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4*>(kt + (local + 16 * i) * kKPitch + part * 8) = r.k[i];
-    *reinterpret_cast<u32x4*>(vt + (local + 16 * i) * kVPitch + part * 8) = r.v[i];
-  }
+#pragma clang diagnostic pop
 }
 
 template <int G>
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     float scale_log2, int max_q, int max_ctx, const int2* __restrict__ items, int num_seqs) {
   constexpr int kTokWG = 128 / G;  // query tokens per work-group
   constexpr int kTokW = 32 / G;    // per wavefront
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBufElems];
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // K0 V0 K1 V1
 
   // work item: from the host plan (one per non-empty tile, heaviest first),
   // else from the grid (kv_head, seq, q-tile counted from the end)
@@ -195,29 +195,53 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 
   const int64_t row_bytes = (int64_t)hkv * kHeadDim * 2;
   const int64_t block_bytes = row_bytes * kBlockSize;
-  const int64_t thread_off = (int64_t)(threadIdx.x >> 4) * row_bytes + (int64_t)g * kHeadDim * 2 + (threadIdx.x & 15) * 16;
+  const int head_off = g * kRowBytes;
   const int32_t* bt = block_tables + (int64_t)b * bt_stride;
-  TileRegs regs;
-  fetch_tile(regs, k_cache, v_cache, bt, 0, L, row_bytes, block_bytes, thread_off, num_blocks);
+  // loop-invariant lane offsets (bytes from the tile start) of the rows this lane loads
+  uint32_t gk[4], gv[4];
+  {
+    const int sub = lane >> 4;
+    const int cp = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * wave + 4 * i + sub;
+      gk[i] = (uint32_t)r * (uint32_t)row_bytes + 16 * (cp ^ (r & 15));
+      gv[i] = (uint32_t)r * (uint32_t)row_bytes + 16 * (cp ^ ((4 * r) & 15));
+    }
+  }
+  issue_tile(smem, smem + kTileBytes, k_cache, v_cache, bt[0], 0, L, row_bytes, block_bytes, head_off, num_blocks,
+             gk, gv);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) retire(qreg[kk]);
-  stage_tile(regs, smem);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // per-lane LDS offsets (elements)
-  const int k_rd = perm_row(col) * kKPitch + 8 * half;  // A operand of S^T: K row perm_row(col)
-  // A operand of O^T: V^T via transposing reads; lane group q16 = lane / 16
-  const int q16 = lane >> 4;
-  const int v_rd = (8 * (q16 >> 1) + ((lane & 15) >> 2)) * kVPitch + 16 * (q16 & 1) + 4 * (lane & 3);
+  // per-lane LDS byte offsets of the MFMA operands (swizzle as in issue_tile)
+  int koff[8];  // A of S^T: K row perm_row(col), logical chunk 2 kk + half
+  {
+    const int row = perm_row(col);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) koff[kk] = row * kRowBytes + 16 * ((2 * kk + half) ^ (row & 15));
+  }
+  int voff[4];  // A of O^T via transposing reads: dims 32 dt .. of rows R0 (+ 32 st + 16 qq + 4 hi)
+  {
+    const int q16 = lane >> 4;
+    const int r0 = 8 * (q16 >> 1) + ((lane & 15) >> 2);
+    const int rr = (lane >> 2) & 3;  // r0 % 4: the V swizzle flips chunk bits 2-3 by it
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      voff[dt] = r0 * kRowBytes + 16 * (2 * (q16 & 1) + ((lane & 3) >> 1) + 4 * (dt ^ rr)) + 8 * (lane & 1);
+  }
 
   for (int kt = 0; kt < nkt; ++kt) {
     const bool has_next = kt + 1 < nkt;
-    if (has_next)
-      fetch_tile(regs, k_cache, v_cache, bt, (kt + 1) * kKeysPerTile, L, row_bytes, block_bytes, thread_off,
-                 num_blocks);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-    const uint16_t* kbuf = smem + (kt & 1) * kBufElems;
-    const uint16_t* vbuf = kbuf + kKTileElems;
+    if (has_next) {
+      char* nb = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+      issue_tile(nb, nb + kTileBytes, k_cache, v_cache, bt[((kt + 1) * kKeysPerTile) >> 8], (kt + 1) * kKeysPerTile,
+                 L, row_bytes, block_bytes, head_off, num_blocks, gk, gv);
+    }
+    const char* kbuf = smem + (kt & 1) * 2 * kTileBytes;
+    const char* vbuf = kbuf + kTileBytes;
     const int key0 = kt * kKeysPerTile;
     const bool act0 = wave_live && key0 <= pmax;
     const bool act1 = wave_live && key0 + 32 <= pmax;
@@ -226,12 +250,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         if (st == 1 && !act1) break;
-        const uint16_t* kr = kbuf + 32 * st * kKPitch + k_rd;
-        u32x4 a = *reinterpret_cast<const u32x4*>(kr);
+        const char* kr = kbuf + 32 * st * kRowBytes;
+        u32x4 a = *reinterpret_cast<const u32x4*>(kr + koff[0]);
         s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[0]), f32x16{}, 0, 0, 0);
 #pragma unroll
         for (int kk = 1; kk < 8; ++kk) {
-          a = *reinterpret_cast<const u32x4*>(kr + 16 * kk);
+          a = *reinterpret_cast<const u32x4*>(kr + koff[kk]);
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[st], 0, 0, 0);
         }
       }
@@ -298,9 +322,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           if (st == 1 && !act1) break;
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq) {
-            const uint16_t* vr = vbuf + (32 * st + 16 * qq) * kVPitch + v_rd + 32 * dt;
-            const uint2 lo = lds_read_tr16(vr);
-            const uint2 hi = lds_read_tr16(vr + 4 * kVPitch);
+            const char* vr = vbuf + (32 * st + 16 * qq) * kRowBytes + voff[dt];
+            const uint2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vr));
+            const uint2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vr + 4 * kRowBytes));
             const u32x4 a = {lo.x, lo.y, hi.x, hi.y};
             acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pk[st][qq]), acc_o[dt],
                                                                 0, 0, 0);
@@ -308,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         }
       }
     }
-    if (has_next) stage_tile(regs, smem + ((kt + 1) & 1) * kBufElems);
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of the next tile have landed in LDS
     __syncthreads();
   }
 
