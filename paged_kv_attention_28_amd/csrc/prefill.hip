@@ -32,10 +32,12 @@
 //    reference max moves only when a row max exceeds it by 8, so most tiles
 //    skip rescaling the 64 output accumulators); fully masked 32-key subtiles
 //    above the causal diagonal are skipped.
-//  * K/V of tile i+1 go from the cache straight into LDS
-//    (global_load_lds_dwordx4) while tile i is computed: no registers, no
-//    LDS writes by the wavefronts; two LDS buffers, one wait and one barrier
-//    per tile. Such a load writes lane l's 16 bytes at LDS base + 16 l, so
+//  * K/V of tile i+1 go from the cache straight into LDS (buffer loads with
+//    the lds bit, buffer_load_dwordx4 ... lds: a scalar descriptor per tile
+//    and loop-invariant 32-bit lane offsets) while tile i is computed: no
+//    registers, no LDS writes by the wavefronts; two LDS buffers, one wait
+//    and one barrier per tile. Such a load writes lane l's 16 bytes at LDS
+//    base + 16 l, so
 //    rows cannot be padded; instead the 16-byte chunks of each 256-byte row
 //    are XOR-swizzled (by r % 16 in K, by 4 r % 16 in V), which keeps the
 //    16-byte K reads and the transposing V reads free of bank conflicts.
@@ -77,8 +79,9 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // K and V of keys [key0, key0 + 64) straight from the cache into LDS
-// (global_load_lds_dwordx4: lane l of an instruction writes its 16 bytes at
-// LDS base + 16 l, whatever address it loads). Wavefront w moves rows
+// (buffer_load_dwordx4 with the lds bit: lane l of an instruction writes its
+// 16 bytes at LDS base + 16 l, whatever address it loads; the descriptor
+// bounds the reads to the tile). Wavefront w moves rows
 // 16 w .. 16 w + 15, four rows per instruction. Rows are stored unpadded,
 // with their 16-byte chunks XOR-swizzled so that the operand reads hit
 // distinct banks: physical chunk p of row r holds logical chunk p ^ (r % 16)
@@ -91,16 +94,17 @@ __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* _
   const int wave = threadIdx.x >> 6;
   // wave-uniform start of the tile in both caches; lanes add 32-bit offsets
   const int64_t base = blk * block_bytes + (int64_t)(key0 & (kBlockSize - 1)) * row_bytes + head_off;
-  const char* kb = kc + base;
-  const char* vb = vc + base;
+  const int span = kKeysPerTile * (int)row_bytes;
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0, span, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0, span, 0x00020000);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
   if (key0 + kKeysPerTile <= L) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r0 = 16 * wave + 4 * i;
-      __builtin_amdgcn_global_load_lds(kb + koff[i], (lds_void*)(kbuf + r0 * kRowBytes), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + voff[i], (lds_void*)(vbuf + r0 * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kbuf + r0 * kRowBytes), 16, koff[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vbuf + r0 * kRowBytes), 16, voff[i], 0, 0, 0);
     }
   } else {
     const int lane = threadIdx.x & 63;
@@ -112,8 +116,8 @@ __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* _
       const int r = r0 + sub;
       const int back = r > last ? r - last : 0;  // rows to step back to the last context row
       const uint32_t d = (uint32_t)back * (uint32_t)row_bytes;
-      __builtin_amdgcn_global_load_lds(kb + (koff[i] - d), (lds_void*)(kbuf + r0 * kRowBytes), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + (voff[i] - d), (lds_void*)(vbuf + r0 * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kbuf + r0 * kRowBytes), 16, koff[i] - d, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vbuf + r0 * kRowBytes), 16, voff[i] - d, 0, 0, 0);
     }
   }
 #pragma clang diagnostic pop
