@@ -43,6 +43,10 @@
 //    16-byte K reads and the transposing V reads free of bank conflicts.
 //  * Keys past the context end are clamped to the last context row (a valid,
 //    written row) and masked, so stale cache rows never enter the result.
+//  * The output leaves through LDS: the accumulators hold O^T (a lane owns one
+//    query row, 8-byte runs of dims), so each wavefront stages its 32 rows in
+//    LDS and writes whole 256-byte rows, 16 bytes per lane; stored directly,
+//    every store instruction would touch 32 rows 16 bytes at a time.
 
 #include "common.h"
 
@@ -340,11 +344,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     __syncthreads();
   }
 
-  // epilogue: lane holds O^T[dims dt*32 + 8 (i/4) + 4 half + (i%4)][its query row]
+  // epilogue: lane holds O^T[dims dt*32 + 8 (i/4) + 4 half + (i%4)][its query row]. Each wavefront
+  // stages its 32 rows in LDS (both tile buffers are free after the last barrier; 8 KiB per
+  // wavefront, 16-byte chunks XOR-swizzled by row) and writes whole 256-byte rows.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (row_valid && wave_live) {
+  if (wave_live) {
     const float inv = 1.f / l_tot;
-    uint16_t* op = out + ((int64_t)(q0 + tok) * hq + qhead) * kHeadDim + 4 * half;
+    char* stage = smem + wave * (32 * kRowBytes);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
@@ -352,7 +358,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         u32x2 w;
         w.x = pack_bf16x2(acc_o[dt][4 * rq + 0] * inv, acc_o[dt][4 * rq + 1] * inv);
         w.y = pack_bf16x2(acc_o[dt][4 * rq + 2] * inv, acc_o[dt][4 * rq + 3] * inv);
-        *reinterpret_cast<u32x2*>(op + dt * 32 + 8 * rq) = w;
+        const int chunk = (4 * dt + rq) ^ (col & 15);
+        *reinterpret_cast<u32x2*>(stage + col * kRowBytes + 16 * chunk + 8 * half) = w;
+      }
+    }
+    const int p = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 4 * i + (lane >> 4);  // row of the wavefront
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * kRowBytes + 16 * (p ^ (rr & 15)));
+      const int rw = wave * 32 + rr;
+      const int t = tok_begin + rw / G;
+      if (t < tok_end) {
+        uint16_t* op = out + ((int64_t)(q0 + t) * hq + g * G + (rw % G)) * kHeadDim + 8 * p;
+        *reinterpret_cast<u32x4*>(op) = v;
       }
     }
   }
