@@ -13,10 +13,15 @@ token) per wall-clock step. ``roofline`` reports the decode attention call
 stream against the 8 TB/s HBM peak; ``traffic`` is the HBM bytes per call from
 the committed rocprofv3 counter summary, or null once the kernel changed. ``prefill`` reports the chunked-prefill step (16384-token
 budget) in TFLOP/s of unmasked attention flops against the 2.5 PFLOP/s bf16
-MFMA peak. ``cpu_baseline`` times the fp64 oracle on the same decode step
-on the host before the GPU is initialised.
+MFMA peak, its roofline fraction max(t_MFMA, t_HBM) / t (HBM bytes: q, out and
+the distinct context K/V rows), and the same call launched back to back for
+0.1 s (the shader clock under this load depends on how busy the GPU is kept).
+``hbm_copy_ceiling`` holds torch's own sum and copy over 2 GiB. ``cpu_baseline`` times the
+fp64 oracle on the same decode step on the host (about 10 s of repeats)
+before the GPU is initialised.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-prefill] [--no-graph] [--no-back-to-back]
 """
 
 from __future__ import annotations
@@ -84,7 +89,15 @@ def prefill_work(w: W.Workload) -> dict:
     flops = 4 * w.head_dim * w.num_q_heads * pairs
     tokens = sum(s.seq_len - s.num_cached for s in p.seqs)
     store = tokens * w.num_kv_heads * w.head_dim * 2 * 4
-    return {"flops": flops, "pairs": pairs, "store": store, "tokens": tokens}
+    # q + out + distinct context K/V rows (a shared prefix block's rows count once)
+    rows = set()
+    for s in p.seqs:
+        for pos in range(s.seq_len):
+            rows.add((s.block_table[pos // w.block_size], pos % w.block_size))
+    kv = len(rows) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * tokens * w.num_q_heads * w.head_dim * 2
+    return {"flops": flops, "pairs": pairs, "store": store, "tokens": tokens, "bytes": kv + qo,
+            "kv_rows": len(rows)}
 
 
 # ----------------------------------------------------------------------------
@@ -116,25 +129,28 @@ def cpu_baseline(w: W.Workload) -> dict:
         kc2, vc2 = op.kv_store_ref(kc, vc, kb, vb, slots)
         return op.decode_ref(q, kc2, vc2, bt, ctx, w.scale)
 
+    def timed():  # repeat the step until about 10 s of CPU work (at least 3 runs); mean per step
+        runs, t0 = 0, time.perf_counter()
+        while runs < 3 or (time.perf_counter() - t0 < 10.0 and runs < 40):
+            run()
+            runs += 1
+        return (time.perf_counter() - t0) / runs, runs
+
     cores = 1
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
-            t0 = time.perf_counter()
-            run()
-            dt = time.perf_counter() - t0
+            dt, runs = timed()
     else:
-        t0 = time.perf_counter()
-        run()
-        dt = time.perf_counter() - t0
+        dt, runs = timed()
         cores = os.cpu_count() or 1
     b = decode_bytes(w)
     gbs = (b["attn"] + b["store"]) / dt / 1e9
-    log(f"[bench] cpu baseline: oracle step {dt:.2f}s -> {gbs:.4f} GB/s")
+    log(f"[bench] cpu baseline: oracle step {dt:.2f}s (mean of {runs}) -> {gbs:.4f} GB/s")
     return {"value": round(gbs, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": "one full decode step of the decode workload (store of 272 rows + decode of 256 "
-                      "sequences and 16 padding rows), fp64 numpy oracle, BLAS limited to 1 thread; "
-                      "host-generated values of the same shapes"}
+            "seconds": round(dt, 3), "runs": runs,
+            "sample": f"one full decode step of the decode workload (store of 272 rows + decode of 256 "
+                      f"sequences and 16 padding rows), repeated {runs} times (about 10 s), fp64 numpy oracle, "
+                      f"BLAS limited to 1 thread; host-generated values of the same shapes"}
 
 
 # ----------------------------------------------------------------------------
@@ -194,6 +210,52 @@ def rope_store_rate(torch, w, runner, reps: int):
         f"({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
     return {"tokens": int(pos.size), "us": round(us, 2), "gbs": round(gbs, 1),
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "bytes_per_token": per_tok}
+
+
+def copy_ceiling(torch, dev, reps: int = 10) -> dict:
+    """Plain torch streaming kernels over 2 GiB on the device, a read-only sum and a copy: the HBM rates that
+    library kernels reach on this machine, reported beside the 8 TB/s vendor figure."""
+    n = 2 * 2**30
+    x = torch.empty(n // 4, dtype=torch.int32, device=dev)
+    x.fill_(1)
+    y = torch.empty_like(x)
+    out = {"bytes": n}
+    for name, fn, moved in (("sum", lambda: x.sum(), n), ("copy", lambda: y.copy_(x), 2 * n)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        gbs = moved / (us * 1e-6) / 1e9
+        log(f"[bench] torch {name} over 2 GiB: {us:.0f} us -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+        out[name] = {"us": round(us, 1), "gbs": round(gbs, 1)}
+    del x, y
+    return out
+
+
+def back_to_back(torch, runner, seconds: float = 0.1) -> float:
+    """Mean time of the attention call launched back to back for about `seconds` (the GPU never idles, so the
+    shader clock settles), after the timed steps."""
+    runner.attention_only()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        runner.attention_only()
+    e1.record()
+    torch.cuda.synchronize()
+    reps = max(10, int(seconds / (e0.elapsed_time(e1) / 10 * 1e-3)))
+    e0.record()
+    for _ in range(reps):
+        runner.attention_only()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def sampler_rate(torch, dev, reps: int = 20):
@@ -291,6 +353,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-back-to-back", action="store_true",
+                    help="skip the 0.1 s back-to-back prefill run (keeps a kernel trace to the timed steps)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; multi-GPU runs are not supported (got --gpus {args.gpus})",
@@ -341,6 +405,21 @@ def main():
         log(f"[bench] prefill step {pms * 1e3:.1f} us wall; store {pstore.mean() * 1e3:.1f} us "
             f"({store_gbs:.0f} GB/s), attention {pav * 1e3:.1f} us -> {tflops:.1f} TFLOP/s "
             f"({tflops / BF16_PEAK_TFLOPS:.1%} of bf16 MFMA peak)")
+        t_mfma = pw["flops"] / (BF16_PEAK_TFLOPS * 1e12)
+        t_hbm = pw["bytes"] / (HBM_PEAK_GBS * 1e9)
+        roof = max(t_mfma, t_hbm) / (pav * 1e-3)
+        log(f"[bench] prefill roofline: t_mfma {t_mfma * 1e6:.1f} us, t_hbm {t_hbm * 1e6:.1f} us "
+            f"({pw['bytes'] / 1e9:.3f} GB: q + out + {pw['kv_rows']} distinct K/V rows) -> "
+            f"max / t = {roof:.1%}")
+        b2b_line = None
+        if not args.no_back_to_back:
+            b2b = back_to_back(torch, rp)
+            b2b_tflops = pw["flops"] / (b2b * 1e-3) / 1e12
+            log(f"[bench] prefill attention back to back for 0.1 s: {b2b * 1e3:.1f} us -> {b2b_tflops:.1f} "
+                f"TFLOP/s ({b2b_tflops / BF16_PEAK_TFLOPS:.1%})")
+            b2b_line = {"attn_us": round(b2b * 1e3, 2), "tflops": round(b2b_tflops, 2),
+                        "pct_bf16_peak": round(100 * b2b_tflops / BF16_PEAK_TFLOPS, 2),
+                        "note": "the same call launched back to back for 0.1 s after the timed steps"}
         rope = rope_store_rate(torch, wp, rp, max(args.steps // 2, 5))
         prefill = {"workload": "chunked prefill: 36 seqs, 16124 new tokens (budget 16384), prompts U[100,1024], "
                                "about half with a shared 256/512-token cached prefix, first seq a mid-block chunk "
@@ -348,10 +427,15 @@ def main():
                    "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
                    "attn_us": round(pav * 1e3, 2), "step_us_wall": round(pms * 1e3, 2),
                    "store_us": round(float(pstore.mean()) * 1e3, 2), "store_gbs": round(store_gbs, 1),
-                   "flops": pw["flops"], "pairs": pw["pairs"], "rope_kv_store": rope}
+                   "flops": pw["flops"], "pairs": pw["pairs"], "bytes": pw["bytes"],
+                   "t_mfma_us": round(t_mfma * 1e6, 2), "t_hbm_us": round(t_hbm * 1e6, 2),
+                   "roofline_frac": round(roof, 4),
+                   "back_to_back": b2b_line,
+                   "rope_kv_store": rope}
 
     graph = None if args.no_graph else graph_vs_eager(torch, dev)
     sampler = sampler_rate(torch, dev)
+    copy = copy_ceiling(torch, dev)
 
     line = {
         "metric": "decode attn GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak",
@@ -380,6 +464,7 @@ def main():
         "prefill": prefill,
         "decode_graph": graph,
         "sampler": sampler,
+        "hbm_copy_ceiling": copy,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
