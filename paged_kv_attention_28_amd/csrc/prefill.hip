@@ -18,10 +18,15 @@
 //    land on one XCD and share its L2. Without a plan the grid is (kv_head,
 //    seq, q-tile counted from the end), sized by max_q_len, and work-groups
 //    past a sequence's last tile exit at once.
-//  * Per 64-key tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows
+//  * Per 32-key tile: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows
 //    from LDS, B = the wavefront's 32 query rows held in registers). In the
-//    transposed product each lane holds 32 scores of one query row, so the
+//    transposed product each lane holds 16 scores of one query row, so the
 //    row max and sum need a single cross-lane exchange (lane ^ 32).
+//  * Occupancy: with 32-key tiles the kernel needs 161 VGPRs and 32 KiB of
+//    LDS, so three work-groups (three wavefronts per SIMD) share a CU; the
+//    third wavefront hides the latencies of the LDS operand reads, the MFMA
+//    chains and the per-tile barrier. (The loops also take 64-key tiles,
+//    kSub = 2, at two work-groups per CU: 10 % slower.)
 //  * O^T += V^T P^T, again 32x32x16: B = P taken straight from the S^T
 //    accumulators (rounded to bf16) because the K rows were fed to the first
 //    product in a permuted order (bits 2 and 3 of the row index swapped)
@@ -30,8 +35,8 @@
 //    (ds_read_b64_tr_b16), so V is staged exactly like K.
 //  * fp32 online softmax in the log2 domain with lazy rescaling (the
 //    reference max moves only when a row max exceeds it by 8, so most tiles
-//    skip rescaling the 64 output accumulators); fully masked 32-key subtiles
-//    above the causal diagonal are skipped.
+//    skip rescaling the 64 output accumulators); a wavefront skips the tiles
+//    above its last query row.
 //  * K/V of tile i+1 go from the cache straight into LDS (buffer loads with
 //    the lds bit, buffer_load_dwordx4 ... lds: a scalar descriptor per tile
 //    and loop-invariant 32-bit lane offsets) while tile i is computed: no
@@ -54,9 +59,11 @@ namespace pkv {
 
 namespace {
 
-constexpr int kKeysPerTile = 64;
+constexpr int kKeysPerTile = 32;
+constexpr int kSub = kKeysPerTile / 32;     // 32-key subtiles per tile
+constexpr int kRowsW = kKeysPerTile / 4;    // tile rows each wavefront loads
 constexpr int kRowBytes = kHeadDim * 2;               // one head of one key: 256 B
-constexpr int kTileBytes = kKeysPerTile * kRowBytes;   // a K (or V) tile: 16 KiB, rows unpadded
+constexpr int kTileBytes = kKeysPerTile * kRowBytes;   // a K (or V) tile: 8 KiB, rows unpadded
 constexpr float kNegBig = -1e30f;
 constexpr float kRescaleSlack = 8.f;  // log2 units: the reference max moves only when a row max exceeds it by this
 
@@ -82,11 +89,11 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// K and V of keys [key0, key0 + 64) straight from the cache into LDS
-// (buffer_load_dwordx4 with the lds bit: lane l of an instruction writes its
-// 16 bytes at LDS base + 16 l, whatever address it loads; the descriptor
-// bounds the reads to the tile). Wavefront w moves rows
-// 16 w .. 16 w + 15, four rows per instruction. Rows are stored unpadded,
+// K and V of keys [key0, key0 + kKeysPerTile) straight from the cache into
+// LDS (buffer_load_dwordx4 with the lds bit: lane l of an instruction writes
+// its 16 bytes at LDS base + 16 l, whatever address it loads; the descriptor
+// bounds the reads to the tile). Wavefront w moves rows kRowsW w ..
+// kRowsW (w + 1) - 1, four rows per instruction. Rows are stored unpadded,
 // with their 16-byte chunks XOR-swizzled so that the operand reads hit
 // distinct banks: physical chunk p of row r holds logical chunk p ^ (r % 16)
 // in K and p ^ (4 r % 16) in V. Keys past the context end load its last row.
@@ -105,8 +112,8 @@ __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* _
 #pragma clang diagnostic ignored "-Wold-style-cast"
   if (key0 + kKeysPerTile <= L) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = 16 * wave + 4 * i;
+    for (int i = 0; i < kRowsW / 4; ++i) {
+      const int r0 = kRowsW * wave + 4 * i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kbuf + r0 * kRowBytes), 16, koff[i], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vbuf + r0 * kRowBytes), 16, voff[i], 0, 0, 0);
     }
@@ -115,8 +122,8 @@ __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* _
     const int sub = lane >> 4;
     const int last = L - 1 - key0;  // >= 0: the tile starts inside the context
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = 16 * wave + 4 * i;
+    for (int i = 0; i < kRowsW / 4; ++i) {
+      const int r0 = kRowsW * wave + 4 * i;
       const int r = r0 + sub;
       const int back = r > last ? r - last : 0;  // rows to step back to the last context row
       const uint32_t d = (uint32_t)back * (uint32_t)row_bytes;
@@ -128,14 +135,16 @@ __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* _
 }
 
 template <int G>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(
+__global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
     const int32_t* __restrict__ context_lens, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int bt_stride, int hq, int hkv, int64_t num_blocks,
     float scale_log2, int max_q, int max_ctx, const int2* __restrict__ items, int num_seqs) {
   constexpr int kTokWG = 128 / G;  // query tokens per work-group
   constexpr int kTokW = 32 / G;    // per wavefront
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];  // K0 V0 K1 V1
+  // K0 V0 K1 V1; after the last tile, the output staging (32 rows per wavefront)
+  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes > 4 * 32 * kRowBytes ? 4 * kTileBytes
+                                                                                       : 4 * 32 * kRowBytes];
 
   // work item: from the host plan (one per non-empty tile, heaviest first),
   // else from the grid (kv_head, seq, q-tile counted from the end)
@@ -211,8 +220,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const int sub = lane >> 4;
     const int cp = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * wave + 4 * i + sub;
+    for (int i = 0; i < kRowsW / 4; ++i) {
+      const int r = kRowsW * wave + 4 * i + sub;
       gk[i] = (uint32_t)r * (uint32_t)row_bytes + 16 * (cp ^ (r & 15));
       gv[i] = (uint32_t)r * (uint32_t)row_bytes + 16 * (cp ^ ((4 * r) & 15));
     }
@@ -252,11 +261,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
     const char* vbuf = kbuf + kTileBytes;
     const int key0 = kt * kKeysPerTile;
     const bool act0 = wave_live && key0 <= pmax;
-    const bool act1 = wave_live && key0 + 32 <= pmax;
+    const bool act1 = kSub == 2 && wave_live && key0 + 32 <= pmax;
     if (act0) {
-      f32x16 s[2];
+      f32x16 s[kSub];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < kSub; ++st) {
         if (st == 1 && !act1) break;
         const char* kr = kbuf + 32 * st * kRowBytes;
         u32x4 a = *reinterpret_cast<const u32x4*>(kr + koff[0]);
@@ -267,9 +276,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
           s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[st], 0, 0, 0);
         }
       }
-      if (!act1) {
+      if (kSub == 2 && !act1) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[1][i] = -__builtin_inff();
+        for (int i = 0; i < 16; ++i) s[kSub - 1][i] = -__builtin_inff();
       }
       // Accumulator element i of subtile st holds key
       //   key0 + 32 st + 16 (i >> 3) + 8 half + (i & 7)
@@ -277,14 +286,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
       if (key0 + kKeysPerTile - 1 > pmin) {  // tile crosses the causal diagonal of some row
         const int lim = pos - key0 - 8 * half;  // element visible iff its key offset <= lim
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < kSub; ++st)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
             if (32 * st + 16 * (i >> 3) + (i & 7) > lim) s[st][i] = -__builtin_inff();
       }
       float mx = kNegBig;
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int st = 0; st < kSub; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
@@ -305,9 +314,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
         m_ref = m_new;
       }
       float lsum = 0.f;
-      u32x4 pk[2][2];
+      u32x4 pk[kSub][2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < kSub; ++st) {
         float p[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -326,7 +335,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < kSub; ++st) {
           if (st == 1 && !act1) break;
 #pragma unroll
           for (int qq = 0; qq < 2; ++qq) {
