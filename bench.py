@@ -16,12 +16,14 @@ budget) in TFLOP/s of unmasked attention flops against the 2.5 PFLOP/s bf16
 MFMA peak, its roofline fraction max(t_MFMA, t_HBM) / t (HBM bytes: q, out and
 the distinct context K/V rows), and the same call launched back to back for
 0.1 s (the shader clock under this load depends on how busy the GPU is kept).
-``hbm_copy_ceiling`` is torch's own copy over 2 GiB. ``cpu_baseline`` times the
+``hbm_copy_ceiling`` is torch's own copy over 2 GiB. ``trace_replay`` replays
+the 28-layer scheduler trace (256 requests) and reports decode GB/s, prefill
+TFLOP/s and kernel-only tokens/s from events around each layer's kernels. ``cpu_baseline`` times the
 fp64 oracle on the same decode step on the host (about 10 s of repeats)
 before the GPU is initialised.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-prefill] [--no-graph] [--no-back-to-back]
+                       [--no-prefill] [--no-graph] [--no-back-to-back] [--no-trace]
 """
 
 from __future__ import annotations
@@ -258,6 +260,71 @@ def back_to_back(torch, runner, seconds: float = 0.1) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+def trace_replay(torch) -> dict:
+    """The scheduler-trace workload: 256 requests (prompt and output lengths U[100, 1024]) scheduled by the native
+    scheduler (FCFS prefill-first, 16384-token budget, 512 sequences, 800 blocks per layer, recompute preemption)
+    and replayed over 28 layers of 16 Q / 8 KV heads with fresh seeded q/k/v per step and layer. Kernel time is
+    the sum of HIP events around each layer's store + attention (the q/k/v draws stay outside)."""
+    from workloads import sched as S
+    from paged_kv_attention_28_amd import binding as B
+    from paged_kv_attention_28_amd import harness as H
+    prompts, outputs = S.requests()
+    t0 = time.perf_counter()
+    steps = B.Scheduler(S.POOL_BLOCKS, W.BLOCK_SIZE, S.MAX_NUM_SEQS, S.MAX_BATCHED_TOKENS).run(prompts, outputs)
+    sched_s = time.perf_counter() - t0
+    runner = H.TraceRunner(W.SEEDS[5], S.NUM_LAYERS, S.POOL_BLOCKS)
+    timing = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    runner.run(steps, timing=timing)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    hq, hkv, d = runner.hq, runner.hkv, runner.d
+    attn_us = {"decode": 0.0, "prefill": 0.0}
+    store_us = 0.0
+    work = {"decode": 0, "prefill": 0}
+    stored = 0
+    per_step = {}
+    for i, st in enumerate(steps):
+        if st.kind == "decode":
+            rows = len(st.seq_lens) + st.num_pad
+            per_step[i] = (sum(st.seq_lens) * hkv * d * 2 * 2 + 2 * rows * hq * d * 2, len(st.seq_lens))
+        else:
+            pairs = sum((L - c) * c + (L - c) * (L - c + 1) // 2 for L, c in zip(st.seq_lens, st.num_cached))
+            per_step[i] = (4 * d * hq * pairs, sum(L - c for L, c in zip(st.seq_lens, st.num_cached)))
+    for i, layer, e0, e1, e2 in timing:
+        k = steps[i].kind
+        store_us += e0.elapsed_time(e1) * 1e3
+        attn_us[k] += e1.elapsed_time(e2) * 1e3
+        work[k] += per_step[i][0]
+        stored += per_step[i][1]
+    tokens = int(sum(outputs))
+    kernel_s = (store_us + attn_us["decode"] + attn_us["prefill"]) * 1e-6
+    out = {"workload": f"{len(prompts)} requests, prompts and outputs U[100, 1024], {S.NUM_LAYERS} layers of "
+                       f"16Q/8KV x 128, native scheduler (budget {S.MAX_BATCHED_TOKENS}, {S.MAX_NUM_SEQS} seqs, "
+                       f"{S.POOL_BLOCKS} blocks/layer)",
+           "steps": len(steps), "prefill_steps": sum(st.kind == "prefill" for st in steps),
+           "decode_steps": sum(st.kind == "decode" for st in steps),
+           "preemptions": int(sum(len(st.preempted) for st in steps)), "output_tokens": tokens,
+           "decode_attn_us": round(attn_us["decode"], 1), "prefill_attn_us": round(attn_us["prefill"], 1),
+           "store_us": round(store_us, 1),
+           "decode_gbs": round(work["decode"] / (attn_us["decode"] * 1e-6) / 1e9, 1),
+           "prefill_tflops": round(work["prefill"] / (attn_us["prefill"] * 1e-6) / 1e12, 1),
+           "store_gbs": round(stored * hkv * d * 2 * 4 / (store_us * 1e-6) / 1e9, 1),
+           "kernel_only_tok_s": round(tokens / kernel_s, 1), "replay_wall_s": round(wall, 2),
+           "scheduler_s": round(sched_s, 3),
+           "note": "decode bytes: K/V context rows once + q + out; prefill: unmasked attention flops; store: 8 KiB "
+                   "per token; tok/s = generated tokens / summed store + attention kernel time over all layers"}
+    log(f"[bench] trace replay: {out['steps']} steps ({out['prefill_steps']} prefill, {out['decode_steps']} decode, "
+        f"{out['preemptions']} preemptions) x {S.NUM_LAYERS} layers; decode attention {out['decode_gbs']} GB/s, "
+        f"prefill attention {out['prefill_tflops']} TFLOP/s, store {out['store_gbs']} GB/s; {tokens} tokens in "
+        f"{kernel_s * 1e3:.1f} ms of kernels -> {out['kernel_only_tok_s']:.0f} tok/s kernel-only; "
+        f"replay wall {wall:.1f} s")
+    del runner
+    torch.cuda.empty_cache()
+    return out
+
+
 def sampler_rate(torch, dev, reps: int = 20):
     """sample_temperature on a 256-row decode batch over a 151936-entry
     vocabulary (fp32 logits and Gumbel noise): HIP events per call.
@@ -353,6 +420,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="skip the 28-layer scheduler-trace replay")
     ap.add_argument("--no-back-to-back", action="store_true",
                     help="skip the 0.1 s back-to-back prefill run (keeps a kernel trace to the timed steps)")
     args = ap.parse_args()
@@ -435,6 +503,7 @@ def main():
 
     graph = None if args.no_graph else graph_vs_eager(torch, dev)
     sampler = sampler_rate(torch, dev)
+    trace = None if args.no_trace else trace_replay(torch)
     copy = copy_ceiling(torch, dev)
 
     line = {
@@ -464,6 +533,7 @@ def main():
         "prefill": prefill,
         "decode_graph": graph,
         "sampler": sampler,
+        "trace_replay": trace,
         "hbm_copy_ceiling": copy,
         "cpu_baseline": cpu,
     }

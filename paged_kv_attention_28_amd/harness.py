@@ -217,10 +217,13 @@ class TraceRunner:
         v = W.randn_bf16(self.seed, s, W.TAG_V, (rows, self.hkv, self.d), self.device)
         return q, k, v
 
-    def run(self, steps, keep=None):
+    def run(self, steps, keep=None, timing=None):
         """steps: ``binding.SchedStep`` list (step i has index i). keep:
         {step index: layers} whose attention outputs are returned (on the
-        host) as {(step index, layer): tensor}."""
+        host) as {(step index, layer): tensor}. timing: a list that receives
+        (step index, layer, e0, e1, e2): HIP events recorded on the current
+        stream before the layer's store, between store and attention, and
+        after attention (the q/k/v draws stay outside)."""
         kept = {}
         for i, st in enumerate(steps):
             m = B.pkv_prepare_step(st.seq_lens, st.num_cached, st.block_tables, W.BLOCK_SIZE, self.mb, st.num_pad)
@@ -228,7 +231,12 @@ class TraceRunner:
             for layer in range(self.L):
                 q, k, v = self.values(i, layer, m.num_tokens)
                 kc, vc = self.caches[layer]
+                if timing is not None:
+                    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                    ev[0].record()
                 B.kv_store(k, v, kc, vc, dm.slot_mapping)
+                if timing is not None:
+                    ev[1].record()
                 out = torch.empty_like(q)
                 if st.kind == "decode":
                     B.paged_attn_decode(out, q, kc, vc, dm.block_tables, dm.context_lens, self.scale,
@@ -237,6 +245,9 @@ class TraceRunner:
                     B.paged_attn_prefill_varlen(out, q, dm.cu_seqlens_q, dm.context_lens, kc, vc,
                                                 dm.block_tables, dm.max_q_len, dm.max_context_len, self.scale,
                                                 work_items=dm.work_items)
+                if timing is not None:
+                    ev[2].record()
+                    timing.append((i, layer, ev[0], ev[1], ev[2]))
                 if keep and layer in keep.get(i, ()):
                     kept[(i, layer)] = out.cpu()
         return kept
