@@ -22,7 +22,7 @@
 //    from LDS, B = the wavefront's 32 query rows held in registers). In the
 //    transposed product each lane holds 16 scores of one query row, so the
 //    row max and sum need a single cross-lane exchange (lane ^ 32).
-//  * Occupancy: with 32-key tiles the kernel needs 161 VGPRs and 32 KiB of
+//  * Occupancy: with 32-key tiles the kernel needs 164 VGPRs and 32 KiB of
 //    LDS, so three work-groups (three wavefronts per SIMD) share a CU; the
 //    third wavefront hides the latencies of the LDS operand reads, the MFMA
 //    chains and the per-tile barrier. (The loops also take 64-key tiles,
@@ -48,6 +48,14 @@
 //    16-byte K reads and the transposing V reads free of bank conflicts.
 //  * Keys past the context end are clamped to the last context row (a valid,
 //    written row) and masked, so stale cache rows never enter the result.
+//  * Few vector instructions besides the math: the key loop is unrolled over
+//    its two LDS stages, so each stage's base is an immediate offset of the
+//    operand reads and the tile loads take scalar LDS destinations; the
+//    lane ^ 32 row-max exchange is one v_permlane32_swap (no LDS round trip);
+//    block ids are bounds-checked with one unsigned 32-bit scalar compare.
+//  * K operands are read four ahead of the S^T products (schedule pinned with
+//    sched_group_barrier), and the P V^T products run key-chunk outer, so the
+//    second half of the exponentials overlaps the first four products.
 //  * The output leaves through LDS: the accumulators hold O^T (a lane owns one
 //    query row, 8-byte runs of dims), so each wavefront stages its 32 rows in
 //    LDS and writes whole 256-byte rows, 16 bytes per lane; stored directly,
@@ -79,7 +87,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_b
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
 // 4k + c names row k, 4-element chunk c; lane i receives element i of the
 // group's 4 x 16 block from rows 0..3.
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* __restrict__ p) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
   const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
@@ -88,6 +96,18 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+template <int N>
+struct Stage {
+  static constexpr int value = N;
+};
+
+// max of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip)
+__device__ __forceinline__ float max_lane32(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
 
 // K and V of keys [key0, key0 + kKeysPerTile) straight from the cache into
 // LDS (buffer_load_dwordx4 with the lds bit: lane l of an instruction writes
@@ -98,11 +118,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 // distinct banks: physical chunk p of row r holds logical chunk p ^ (r % 16)
 // in K and p ^ (4 r % 16) in V. Keys past the context end load its last row.
 __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* __restrict__ kc,
-                                           const char* __restrict__ vc, int64_t blk, int key0, int L,
+                                           const char* __restrict__ vc, int32_t blk32, int key0, int L,
                                            int64_t row_bytes, int64_t block_bytes, int head_off,
-                                           int64_t num_blocks, const uint32_t (&koff)[4], const uint32_t (&voff)[4]) {
-  if (blk < 0 || blk >= num_blocks) blk = 0;  // caller error: stay inside the pool
-  const int wave = threadIdx.x >> 6;
+                                           uint32_t num_blocks32, int wave, const uint32_t (&koff)[4],
+                                           const uint32_t (&voff)[4]) {
+  // caller error: stay inside the pool (one unsigned compare also rejects negative ids)
+  const int64_t blk = (uint32_t)blk32 < num_blocks32 ? (int64_t)(uint32_t)blk32 : 0;
   // wave-uniform start of the tile in both caches; lanes add 32-bit offsets
   const int64_t base = blk * block_bytes + (int64_t)(key0 & (kBlockSize - 1)) * row_bytes + head_off;
   const int span = kKeysPerTile * (int)row_bytes;
@@ -226,7 +247,8 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
       gv[i] = (uint32_t)r * (uint32_t)row_bytes + 16 * (cp ^ ((4 * r) & 15));
     }
   }
-  issue_tile(smem, smem + kTileBytes, k_cache, v_cache, bt[0], 0, L, row_bytes, block_bytes, head_off, num_blocks,
+  const uint32_t nblk32 = num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)num_blocks;
+  issue_tile(smem, smem + kTileBytes, k_cache, v_cache, bt[0], 0, L, row_bytes, block_bytes, head_off, nblk32, wave,
              gk, gv);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) retire(qreg[kk]);
@@ -250,14 +272,17 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
       voff[dt] = r0 * kRowBytes + 16 * (2 * (q16 & 1) + ((lane & 3) >> 1) + 4 * (dt ^ rr)) + 8 * (lane & 1);
   }
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // one key tile; the LDS stage is a compile-time constant so that operand
+  // addresses fold the stage base into the instructions' offset fields
+  auto key_tile = [&](auto stage_c, const int kt) {
+    constexpr int stg = decltype(stage_c)::value;
     const bool has_next = kt + 1 < nkt;
     if (has_next) {
-      char* nb = smem + ((kt + 1) & 1) * 2 * kTileBytes;
+      char* nb = smem + (1 - stg) * 2 * kTileBytes;
       issue_tile(nb, nb + kTileBytes, k_cache, v_cache, bt[((kt + 1) * kKeysPerTile) >> 8], (kt + 1) * kKeysPerTile,
-                 L, row_bytes, block_bytes, head_off, num_blocks, gk, gv);
+                 L, row_bytes, block_bytes, head_off, nblk32, wave, gk, gv);
     }
-    const char* kbuf = smem + (kt & 1) * 2 * kTileBytes;
+    const char* kbuf = smem + stg * 2 * kTileBytes;
     const char* vbuf = kbuf + kTileBytes;
     const int key0 = kt * kKeysPerTile;
     const bool act0 = wave_live && key0 <= pmax;
@@ -268,13 +293,25 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
       for (int st = 0; st < kSub; ++st) {
         if (st == 1 && !act1) break;
         const char* kr = kbuf + 32 * st * kRowBytes;
-        u32x4 a = *reinterpret_cast<const u32x4*>(kr + koff[0]);
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[0]), f32x16{}, 0, 0, 0);
+        // K operands four reads ahead of the products that use them
+        u32x4 a[4];
 #pragma unroll
-        for (int kk = 1; kk < 8; ++kk) {
-          a = *reinterpret_cast<const u32x4*>(kr + koff[kk]);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[st], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const u32x4*>(kr + koff[kk]);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const u32x4 cur = a[kk & 3];
+          if (kk + 4 < 8) a[kk & 3] = *reinterpret_cast<const u32x4*>(kr + koff[kk + 4]);
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qreg[kk]),
+                                                          kk == 0 ? f32x16{} : s[st], 0, 0, 0);
         }
+        // keep the schedule: four reads, then product / next read pairs, then the last four products
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
       if (kSub == 2 && !act1) {
 #pragma unroll
@@ -296,7 +333,7 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
       for (int st = 0; st < kSub; ++st)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+      mx = max_lane32(mx) * scale_log2;
       // Lazy rescale: exponents are taken against m_ref, which moves (and
       // rescales this row's running sums) only when the row max exceeds it
       // by more than kRescaleSlack, so weights stay <= 2^slack. The decision
@@ -313,7 +350,7 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
           for (int i = 0; i < 16; ++i) acc_o[dt][i] *= alpha;
         m_ref = m_new;
       }
-      float lsum = 0.f;
+      float lsum = -0.f;  // -0 + x == x exactly, so the first add folds away
       u32x4 pk[kSub][2];
 #pragma unroll
       for (int st = 0; st < kSub; ++st) {
@@ -333,12 +370,15 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
       }
       l_run += lsum;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
+      // key chunk outer, output dims inner: the four products of the first 16
+      // keys need only the first half of the weights, so the second half's
+      // exponentials can run while they execute
+      for (int st = 0; st < kSub; ++st) {
+        if (st == 1 && !act1) break;
 #pragma unroll
-        for (int st = 0; st < kSub; ++st) {
-          if (st == 1 && !act1) break;
+        for (int qq = 0; qq < 2; ++qq) {
 #pragma unroll
-          for (int qq = 0; qq < 2; ++qq) {
+          for (int dt = 0; dt < 4; ++dt) {
             const char* vr = vbuf + (32 * st + 16 * qq) * kRowBytes + voff[dt];
             const uint2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vr));
             const uint2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vr + 4 * kRowBytes));
@@ -351,6 +391,10 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of the next tile have landed in LDS
     __syncthreads();
+  };
+  for (int kt = 0; kt < nkt; kt += 2) {
+    key_tile(Stage<0>{}, kt);
+    if (kt + 1 < nkt) key_tile(Stage<1>{}, kt + 1);
   }
 
   // epilogue: lane holds O^T[dims dt*32 + 8 (i/4) + 4 half + (i%4)][its query row]. Each wavefront
