@@ -10,10 +10,12 @@
 // Each operation is one correctly rounded fp32 operation (no fused
 // multiply-add), so the choice is reproducible off the device.
 //
-// HBM-bound: 8 bytes (logit + noise) per vocabulary entry. Pass 1 splits each
-// row over enough work-groups to fill the chip and writes each chunk's best
-// (key, index) to the workspace; pass 2 reduces a row's chunks in one
-// wavefront. No atomics: the result is deterministic.
+// HBM-bound: 8 bytes (logit + noise) per vocabulary entry. Pass 1 splits the
+// rows over about three work-groups per CU, each thread keeping four steps of
+// nontemporal 16-byte loads in flight (the rows are read once), and writes
+// each chunk's best (key, index) to the workspace; pass 2 reduces a row's
+// chunks in one wavefront. No atomics: the result is deterministic, and the
+// first-index tie-break makes it independent of the visiting order.
 
 #include "common.h"
 
@@ -44,6 +46,11 @@ __device__ __forceinline__ Best wave_best(Best b) {
 }
 
 constexpr int kThreads = 256;
+// Work-groups per call. Measured on 256 x 151,936 logits: 512-768 work-groups,
+// each thread with four steps of nontemporal loads in flight, read 2x faster
+// than 2048 work-groups with one step in flight when the caches hold dirty
+// lines (59.7 vs 119 us) and 2 % faster back to back (52.1 vs 53.0 us).
+constexpr int kTargetWgs = 768;
 
 __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(const float* __restrict__ logits, int64_t lstride,
                                                                 const float* __restrict__ temps,
@@ -59,7 +66,30 @@ __global__ __launch_bounds__(kThreads) void sample_chunk_kernel(const float* __r
   Best b{-__builtin_inff(), c0};
   // 16-byte loads over the 4-aligned body of the chunk (chunk is a multiple of 4)
   const int body = c0 + ((c1 - c0) & ~3);
-  for (int j = c0 + 4 * (int)threadIdx.x; j < body; j += 4 * kThreads) {
+  int j = c0 + 4 * (int)threadIdx.x;
+  // four steps' loads in flight before any is used
+  for (; j + 3 * 4 * kThreads < body; j += 4 * 4 * kThreads) {
+    f32x4 l[4], g[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      l[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lr + j + u * 4 * kThreads));
+      g[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(gr + j + u * 4 * kThreads));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = j + u * 4 * kThreads + e;
+        const float prod = l[u][e] * inv;
+        const float k = prod + g[u][e];
+        if (better(k, jj, b.key, b.idx)) {
+          b.key = k;
+          b.idx = jj;
+        }
+      }
+    }
+  }
+  for (; j < body; j += 4 * kThreads) {
     const f32x4 l = *reinterpret_cast<const f32x4*>(lr + j);
     const f32x4 g = *reinterpret_cast<const f32x4*>(gr + j);
 #pragma unroll
@@ -107,9 +137,9 @@ __global__ __launch_bounds__(64) void sample_reduce_kernel(const float2* __restr
   if (threadIdx.x == 0) out[row] = b.idx;
 }
 
-// chunks per row: enough work-groups for the whole chip, at least 4096 entries each
+// chunks per row: about kTargetWgs work-groups in all (three per CU), at least 4096 entries each
 int splits_for(int32_t rows, int32_t vocab, int* chunk) {
-  int s = (2048 + rows - 1) / rows;
+  int s = (kTargetWgs + rows - 1) / rows;
   const int max_s = (vocab + 4095) / 4096;
   s = s < 1 ? 1 : (s > max_s ? max_s : s);
   int c = (vocab + s - 1) / s;
