@@ -369,10 +369,10 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
         }
       }
       l_run += lsum;
-#pragma unroll
       // key chunk outer, output dims inner: the four products of the first 16
       // keys need only the first half of the weights, so the second half's
       // exponentials can run while they execute
+#pragma unroll
       for (int st = 0; st < kSub; ++st) {
         if (st == 1 && !act1) break;
 #pragma unroll
