@@ -164,8 +164,9 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * Supported: head_dim 128, block_size 256, num_kv_heads in {1, 2, 4, 8},
  * num_q_heads / num_kv_heads in {1, 2, 4, 8}, num_seqs <= 8192.
  * Results are deterministic: the split of the work depends only on the
- * context lengths and the device's CU count (one work-group of four
- * wavefronts per CU on 7/8 of the CUs), and partial results are combined in
+ * context lengths, max_context_len and the device's CU count (one
+ * work-group of four wavefronts per CU on 3/4 of the CUs when
+ * max_context_len <= 4096, else 7/8), and partial results are combined in
  * a fixed order (no atomics).
  */
 pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,

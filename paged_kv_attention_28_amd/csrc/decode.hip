@@ -22,8 +22,9 @@
 //    divided evenly over all wavefronts of a persistent grid, so
 //    there are no empty work-groups and no tail of unequal splits. The grid
 //    is one work-group per CU (the launch reserves enough LDS for that), i.e.
-//    one wavefront per SIMD, on 7/8 of the CUs: fewer, longer ranges than the
-//    two per SIMD the registers would allow, which streams faster. A
+//    one wavefront per SIMD, on 3/4 of the CUs for contexts up to 4096 and
+//    7/8 beyond: fewer, longer ranges than the two per SIMD the registers
+//    would allow, which streams faster. A
 //    wavefront walks its range across sequence boundaries with the loads of
 //    the next step always in flight (two register buffers; block-table rows
 //    and the next sequence's queries are prefetched). K/V loads are
@@ -645,11 +646,12 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
   float* part_o = reinterpret_cast<float*>(wsb + lo.header_bytes + lo.ml_bytes);
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = stream_lds(num_seqs);
-  // 7/8 of the CUs: measured on MI355X (256 CUs) over 128..256 work-groups, 224 was at or near the fastest on
-  // the 256-sequence decode (3.7 % faster than 256), 64 sequences (5 %) and long contexts (2.5 %).
+  // Part of the CUs, by the caller's bound on the context: measured on MI355X (256 CUs) over 128..256
+  // work-groups, contexts up to 2048 ran fastest on 176-192 (192 against 256: 5.6 % on 256 sequences, 6 % on
+  // 64) and contexts of 4096-32768 on 224 (2.5 % against 256; 192 was 10 % slower there).
   const int resident = resident_wgs(pick_kernel(G, num_kv_heads), lds);
   if (resident <= 0) return fail(PKV_ERR_HIP, "paged_attn_decode: cannot query the device");
-  const int grid = resident >= 8 ? resident * 7 / 8 : resident;
+  const int grid = resident < 8 ? resident : (max_context_len <= 4096 ? resident * 3 / 4 : resident * 7 / 8);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
