@@ -3,6 +3,8 @@
 A step is one pass of the whole path over one batch, as an engine runs it:
 host step preparation (slot mapping, lengths, padded block tables) into
 pinned buffers, upload, kv_store of the step's K/V, then attention.
+``decode_step_fused`` times the same decode step with the store inside the
+attention call (paged_attn_decode_store).
 
 Headline (``value``): the decode step of the 256-sequence decode workload
 (contexts U[100, 2048], 16 Q / 8 KV heads, head dim 128, bf16, block 256,
@@ -23,7 +25,7 @@ fp64 oracle on the same decode step on the host (about 10 s of repeats)
 before the GPU is initialised.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-prefill] [--no-graph] [--no-back-to-back] [--no-trace]
+                       [--no-prefill] [--no-graph] [--no-back-to-back] [--no-trace] [--no-fused]
 """
 
 from __future__ import annotations
@@ -181,6 +183,27 @@ def time_steps(runner, steps: int, warmup: int, torch):
     store_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     attn_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     return wall / steps * 1e3, store_ms, attn_ms
+
+
+def fused_steps(runner, steps: int, warmup: int, torch):
+    """The decode step with the store fused into the attention call
+    (paged_attn_decode_store): wall-clock per step over `steps` steps and the
+    mean HIP-event time of the call on its stream."""
+    for _ in range(warmup):
+        runner.prepare_and_upload()
+        runner.fused_only()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        runner.prepare_and_upload()
+        evs[i][0].record()
+        runner.fused_only()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    return wall / steps * 1e3, float(call_ms.mean())
 
 
 def rope_store_rate(torch, w, runner, reps: int):
@@ -421,6 +444,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the 28-layer scheduler-trace replay")
+    ap.add_argument("--no-fused", action="store_true", help="skip the decode step with the store fused")
     ap.add_argument("--no-back-to-back", action="store_true",
                     help="skip the 0.1 s back-to-back prefill run (keeps a kernel trace to the timed steps)")
     args = ap.parse_args()
@@ -456,6 +480,14 @@ def main():
     achieved = db["attn"] / (attn_avg * 1e-3) / 1e9
     log(f"[bench] decode step {ms * 1e3:.1f} us wall; store {store_ms.mean() * 1e3:.1f} us, "
         f"attention {attn_avg * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
+    fused = None
+    if not args.no_fused:
+        fms, fcall = fused_steps(runner, args.steps, args.warmup, torch)
+        fused = {"ms_per_step": round(fms, 5), "gbs": round(step_bytes / (fms * 1e-3) / 1e9, 1),
+                 "call_us": round(fcall * 1e3, 2),
+                 "note": "the same decode step with the store fused into the attention call "
+                         "(paged_attn_decode_store)"}
+        log(f"[bench] decode step with the store fused: {fms * 1e3:.1f} us wall; call {fcall * 1e3:.1f} us")
 
     # ---- prefill step ----
     prefill = None
@@ -530,6 +562,7 @@ def main():
                                "on its stream, mean over the timed steps",
                      "algorithmic_bytes": db["attn"], "us": round(attn_avg * 1e3, 2)},
         "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
+        "decode_step_fused": fused,
         "prefill": prefill,
         "decode_graph": graph,
         "sampler": sampler,

@@ -59,7 +59,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 6
+#define PKV_ABI_VERSION 7
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -175,6 +175,39 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int64_t num_blocks, float scale, int32_t max_context_len,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_store — kv_store of the step's new token followed by
+ * paged_attn_decode, in one launch (P1, "第六站：注意力层": each step stores
+ * the new token's K/V before attention reads the context through the block
+ * table). Results equal those two calls bit for bit: the new token, at
+ * position context_lens[s] - 1, is read from key/value row s instead of the
+ * cache, and the wavefront that reads it also writes it to cache row
+ * slot_mapping[s]; no other position of the call reads that row.
+ *
+ *   key, value       device bf16 [num_seqs, num_kv_heads, head_dim]; row s
+ *                    (token stride in elements, 16-byte aligned rows) is the
+ *                    K/V of sequence s's new token
+ *   slot_mapping     device int32 [num_seqs]; the cache row of position
+ *                    context_lens[s] - 1 in sequence s's block table, or -1
+ *                    (padding rows, context 0) to store nothing; a slot
+ *                    outside the pool is skipped
+ *   k_cache, v_cache written at the slots' rows and read elsewhere
+ *   other arguments  as for paged_attn_decode (same workspace size)
+ * Errors: as for paged_attn_decode, plus PKV_ERR_INVALID for null
+ * key/value/slot_mapping or a token stride below a row, and
+ * PKV_ERR_UNSUPPORTED for rows not 16-byte aligned. Slots that disagree with
+ * the block tables are the caller's error (the attention then uses the new
+ * row while the cache receives it elsewhere).
+ */
+pkv_status paged_attn_decode_store(void* out, const void* q, const void* key, int64_t key_token_stride,
+                                   const void* value, int64_t value_token_stride,
+                                   const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, int32_t block_table_stride,
+                                   const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                   int64_t num_blocks, float scale, int32_t max_context_len,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_attn_prefill_varlen — causal attention for a batch of variable-length

@@ -20,12 +20,13 @@ PKV_OK = 0
 STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "HIP", 4: "WORKSPACE"}
 
 EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
-           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_prefill_varlen",
+           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_store",
+           "paged_attn_prefill_varlen",
            "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
            "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks", "pkv_decode_graphs_create",
            "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy", "rope_kv_store", "pkv_rope_cos_sin",
            "sample_temperature_workspace_size", "sample_temperature")
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class PkvError(RuntimeError):
@@ -86,6 +87,10 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode.restype = c_i32
     lib.paged_attn_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                       c_i64, c_f32, c_i32, c_vp, c_size, c_vp]
+    lib.paged_attn_decode_store.restype = c_i32
+    lib.paged_attn_decode_store.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
+                                            c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_f32, c_i32, c_vp, c_size,
+                                            c_vp]
     lib.paged_attn_prefill_varlen.restype = c_i32
     lib.paged_attn_prefill_varlen.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                               c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_f32, c_vp, c_i32,
@@ -433,6 +438,40 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
                                _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, N,
                                float(scale), int(max_context_len), ws_ptr, ws_bytes, _stream(stream))
     _check("paged_attn_decode", st)
+
+
+def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale,
+                            max_context_len, workspace=None, stream=None):
+    """kv_store of the new tokens and paged_attn_decode in one call. key/value
+    [S, H_kv, D] bf16 (row s: sequence s's new token, token stride may exceed
+    a row); slot_mapping [S] int32 (cache row of position context_lens[s] - 1,
+    -1 for padding rows); the rest as for paged_attn_decode."""
+    torch = _torch()
+    lib = load_library()
+    S, Hq, D = q.shape
+    N, B, Hkv, _ = k_cache.shape
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] < S or context_lens.shape[0] < S:
+        raise ValueError("block_tables / context_lens do not cover the batch")
+    if key.shape[0] < S or value.shape[0] < S or slot_mapping.shape[0] < S:
+        raise ValueError("key, value and slot_mapping must cover the batch")
+    for t, n in ((key, "key"), (value, "value")):
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{n} rows must be contiguous [H_kv, D]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace", workspace.dtype)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.paged_attn_decode_store(_dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+                                     _dev(key, "key", torch.bfloat16, False), key.stride(0),
+                                     _dev(value, "value", torch.bfloat16, False), value.stride(0),
+                                     _dev(slot_mapping, "slot_mapping", torch.int32),
+                                     _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+                                     _dev(block_tables, "block_tables", torch.int32), block_tables.stride(0),
+                                     _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, N,
+                                     float(scale), int(max_context_len), ws_ptr, ws_bytes, _stream(stream))
+    _check("paged_attn_decode_store", st)
 
 
 def paged_attn_prefill_varlen(out, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables, max_q_len,

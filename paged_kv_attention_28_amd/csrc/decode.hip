@@ -113,12 +113,29 @@ struct Step {
   int64_t row0;            // cache row of the step's first token
   int last_valid_row_off;  // context length - 1 - first token of the step (>= 0)
   bool live;               // false for a padding step past the wavefront's range (fully masked)
+  int32_t slot;            // fused store: cache row of the new token on the sequence's last step, else -1
+};
+
+// The step's new K/V rows for the fused store (paged_attn_decode_store): row b
+// of k / v is sequence b's token at position context_lens[b] - 1, read from
+// there instead of the cache and written to cache row slots[b]. k == nullptr
+// when the caller stored the rows beforehand (paged_attn_decode).
+struct NewRows {
+  const char* k;
+  const char* v;
+  int64_t k_stride_b, v_stride_b;  // bytes between sequences' rows
+  const int32_t* slots;
+  int64_t num_slots;
+  char* k_cache;  // the caches, writable (only the slots' rows are written)
+  char* v_cache;
 };
 
 template <int HKV>
 __device__ __forceinline__ void load_buf(Buf& x, const char* __restrict__ kc, const char* __restrict__ vc,
-                                         const Step& st, int grp, int li) {
+                                         const Step& st, int grp, int li, const NewRows& nr) {
   constexpr int TW = 8 / HKV;
+  // wave-uniform: only a sequence's last step holds its new token
+  const bool from_input = nr.k && st.last_valid_row_off < 2 * TW;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     int off = t * TW + grp / HKV;
@@ -126,10 +143,34 @@ __device__ __forceinline__ void load_buf(Buf& x, const char* __restrict__ kc, co
     const int64_t row = (st.row0 + off) * HKV + (grp % HKV);
     const char* kp = kc + row * (kHeadDim * 2) + li * 16;
     const char* vp = vc + row * (kHeadDim * 2) + li * 16;
+    if (from_input && off == st.last_valid_row_off) {  // the new token: from the step's input rows
+      kp = nr.k + (int64_t)st.b * nr.k_stride_b + (grp % HKV) * (kHeadDim * 2) + li * 16;
+      vp = nr.v + (int64_t)st.b * nr.v_stride_b + (grp % HKV) * (kHeadDim * 2) + li * 16;
+    }
     x.k[t][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
     x.k[t][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 128));
     x.v[t][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
     x.v[t][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 128));
+  }
+}
+
+// Fused store: the wavefront whose step holds a sequence's new token writes
+// that token's K/V rows (already in registers) to the cache. Only the lanes
+// whose own, unclamped token is the new one store, so each row is written
+// once; padding steps and slots outside the pool store nothing.
+template <int HKV>
+__device__ __forceinline__ void store_new_row(const Buf& x, const Step& st, const NewRows& nr, int grp, int li) {
+  constexpr int TW = 8 / HKV;
+  const int32_t slot = st.slot;
+  if (!nr.k || !st.live || st.last_valid_row_off >= 2 * TW || slot < 0 || (int64_t)slot >= nr.num_slots) return;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t * TW + grp / HKV != st.last_valid_row_off) continue;
+    const int64_t off = ((int64_t)slot * HKV + grp % HKV) * (kHeadDim * 2) + li * 16;
+    *reinterpret_cast<u32x4*>(nr.k_cache + off) = x.k[t][0];
+    *reinterpret_cast<u32x4*>(nr.k_cache + off + 128) = x.k[t][1];
+    *reinterpret_cast<u32x4*>(nr.v_cache + off) = x.v[t][0];
+    *reinterpret_cast<u32x4*>(nr.v_cache + off + 128) = x.v[t][1];
   }
 }
 
@@ -294,7 +335,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables, int bt_stride,
     const int32_t* __restrict__ context_lens, int num_seqs, int64_t num_blocks, float scale_log2, int max_ctx,
-    int32_t* __restrict__ header, float* __restrict__ part_ml, float* __restrict__ part_o) {
+    int32_t* __restrict__ header, float* __restrict__ part_ml, float* __restrict__ part_o, const NewRows nr) {
   constexpr int TW = 8 / HKV;       // tokens per window (one load covers TW token rows)
   constexpr int STEP_TOK = 2 * TW;  // tokens per step
   constexpr int HQ = G * HKV;
@@ -372,6 +413,8 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     st.row0 = blk * kBlockSize + (tok0 & (kBlockSize - 1));
     st.last_valid_row_off = ld_L - 1 - tok0;
     st.live = true;
+    // fused store: the slot is read when the last step is made, a step before it is used
+    st.slot = (nr.k && st.last_valid_row_off < STEP_TOK) ? nr.slots[ld_b] : -1;
     return st;
   };
   auto advance_load = [&]() {
@@ -490,7 +533,7 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 
   Buf A, B;
   Step sa = make_step();
-  load_buf<HKV>(A, k_cache, v_cache, sa, grp, li);
+  load_buf<HKV>(A, k_cache, v_cache, sa, grp, li, nr);
   advance_load();
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -503,17 +546,19 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
     // so they are never sunk below the compute of the current step.
     const bool hasB = gi + 1 < s1;
     const Step sb = hasB ? make_step() : padding_step(sa);
-    load_buf<HKV>(B, k_cache, v_cache, sb, grp, li);
+    load_buf<HKV>(B, k_cache, v_cache, sb, grp, li, nr);
     if (hasB) advance_load();
     __builtin_amdgcn_sched_barrier(0);
     compute_buf<G, HKV>(S, A, qa, qb, sa, grp, scale_log2);
+    store_new_row<HKV>(A, sa, nr, grp, li);
     if (ends_piece(sa, gi)) finish_piece(sa, gi);
     const bool hasA = gi + 2 < s1;
     const Step sn = hasA ? make_step() : padding_step(sb);
-    load_buf<HKV>(A, k_cache, v_cache, sn, grp, li);
+    load_buf<HKV>(A, k_cache, v_cache, sn, grp, li, nr);
     if (hasA) advance_load();
     __builtin_amdgcn_sched_barrier(0);
     compute_buf<G, HKV>(S, B, qa, qb, sb, grp, scale_log2);
+    if (hasB) store_new_row<HKV>(B, sb, nr, grp, li);
     if (hasB && ends_piece(sb, gi + 1)) finish_piece(sb, gi + 1);
     sa = sn;
   }
@@ -602,13 +647,14 @@ extern "C" size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num
   return lo.header_bytes + lo.ml_bytes + lo.o_bytes;
 }
 
-extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                                        const int32_t* block_tables, int32_t block_table_stride,
-                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
-                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                        int64_t num_blocks, float scale, int32_t max_context_len, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
-  using namespace pkv;
+namespace pkv {
+namespace {
+
+pkv_status decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int64_t num_blocks, float scale, int32_t max_context_len, void* workspace,
+                       size_t workspace_bytes, void* stream, const NewRows& nr) {
   if (num_seqs < 0 || num_blocks < 0 || max_context_len < 0 || block_table_stride < 0)
     return fail(PKV_ERR_INVALID, "paged_attn_decode: negative size");
   if (head_dim != kHeadDim) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: head_dim %d (128 only)", head_dim);
@@ -660,7 +706,7 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
 #define PKV_DECODE_LAUNCH(GG, HH)                                                                         \
   hipLaunchKernelGGL((decode_stream_kernel<GG, HH>), dim3(grid), dim3(256), lds, s, o, qq, kc, vc,       \
                      block_tables, block_table_stride, context_lens, num_seqs, num_blocks, scale_log2,   \
-                     max_context_len, header, part_ml, part_o)
+                     max_context_len, header, part_ml, part_o, nr)
 #define PKV_DECODE_HKV(GG)                    \
   switch (num_kv_heads) {                     \
     case 1: PKV_DECODE_LAUNCH(GG, 1); break;  \
@@ -689,4 +735,49 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
     default: return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d query heads", num_q_heads);
   }
   return check_launch("paged_attn_decode (merge)");
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t block_table_stride,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int64_t num_blocks, float scale, int32_t max_context_len, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  const pkv::NewRows none{nullptr, nullptr, 0, 0, nullptr, 0, nullptr, nullptr};
+  return pkv::decode_call(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, max_context_len,
+                          workspace, workspace_bytes, stream, none);
+}
+
+extern "C" pkv_status paged_attn_decode_store(void* out, const void* q, const void* key, int64_t key_token_stride,
+                                              const void* value, int64_t value_token_stride,
+                                              const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                              const int32_t* block_tables, int32_t block_table_stride,
+                                              const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int64_t num_blocks, float scale, int32_t max_context_len,
+                                              void* workspace, size_t workspace_bytes, void* stream) {
+  using namespace pkv;
+  if (num_seqs > 0) {
+    if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID, "paged_attn_decode_store: null pointer");
+    if (head_dim != kHeadDim)
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode_store: head_dim %d (128 only)", head_dim);
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (key_token_stride < row || value_token_stride < row)
+      return fail(PKV_ERR_INVALID, "paged_attn_decode_store: token stride smaller than a row (%lld elements)",
+                  (long long)row);
+    if ((key_token_stride * 2) % 16 || (value_token_stride * 2) % 16 || !aligned16(key) || !aligned16(value))
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode_store: key/value and their strides must be 16-byte aligned");
+    if (num_blocks > INT64_MAX / block_size || block_size <= 0)
+      return fail(PKV_ERR_INVALID, "paged_attn_decode_store: num_blocks or block_size out of range");
+  }
+  const NewRows nr{static_cast<const char*>(key), static_cast<const char*>(value), key_token_stride * 2,
+                   value_token_stride * 2, slot_mapping, num_blocks * (block_size > 0 ? block_size : 1),
+                   static_cast<char*>(k_cache), static_cast<char*>(v_cache)};
+  return decode_call(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, scale, max_context_len, workspace,
+                     workspace_bytes, stream, nr);
 }

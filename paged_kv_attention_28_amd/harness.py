@@ -181,6 +181,14 @@ class StepRunner:
             B.paged_attn_prefill_varlen(self.out, self.q, cu, ctx, self.dw.k_cache, self.dw.v_cache, bt2,
                                         self.max_q_len, self.max_ctx, w.scale, work_items=items)
 
+    def fused_only(self):
+        """Decode passes: the store and the attention in one call (paged_attn_decode_store)."""
+        w = self.dw.w
+        slots, _, ctx, bt = self.dev_meta
+        bt2 = bt.view(-1, w.max_blocks_per_seq)
+        B.paged_attn_decode_store(self.out, self.q, self.k, self.v, slots, self.dw.k_cache, self.dw.v_cache, bt2, ctx,
+                                  w.scale, self.max_ctx, self.workspace)
+
     def kernels(self):
         self.store_only()
         self.attention_only()

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(P.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_abi_version() == 6
+    assert lib.pkv_abi_version() == 7
 
 
 def test_product_package_does_not_import_oracle():
@@ -152,6 +152,20 @@ def test_decode_validation(lib):
     assert lib.paged_attn_decode(*args(wsb=16)) == 4         # workspace too small
     assert lib.paged_attn_decode(*args(ws=F + 16)) == 2      # workspace misaligned
     assert lib.paged_attn_decode(*args(S=0)) == 0
+
+
+def test_decode_store_validation(lib):
+    """Host checks of the fused store + decode call (every case fails before a launch, or does nothing)."""
+    args = lambda **kw: [F, F, kw.get("key", F), kw.get("ks", 1024), F, kw.get("vs", 1024), kw.get("slots", F), F, F,
+                         F, 8, F, kw.get("S", 4), 16, 8, kw.get("d", 128), 256, 100, 0.088, 2048, F, 1 << 30, None]
+    assert lib.paged_attn_decode_store(*args(key=None)) == 1
+    assert "null" in P.last_error()
+    assert lib.paged_attn_decode_store(*args(slots=None)) == 1
+    assert lib.paged_attn_decode_store(*args(ks=1000)) == 1          # stride < row
+    assert lib.paged_attn_decode_store(*args(vs=1028)) == 2          # stride not 16-byte aligned
+    assert lib.paged_attn_decode_store(*args(key=F + 8)) == 2        # key not 16-byte aligned
+    assert lib.paged_attn_decode_store(*args(d=64)) == 2
+    assert lib.paged_attn_decode_store(*args(S=0, key=None)) == 0    # nothing to do
 
 
 def test_prefill_validation(lib):
