@@ -300,6 +300,65 @@ def test_block_relabel_bit_identical():
         assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), kind
 
 
+BIG_POOL = 8704  # 8704 blocks x 512 KiB = 4.56 GB per cache: blocks from 8192 on start past 2^32 bytes
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_blocks_past_4gib(kind):
+    """Every block moved to an id >= 8192 of an 8704-block pool, so each cache byte offset
+    exceeds 2^32: kv_store, the fused decode store and both attention launches give the bits
+    of the same work on a compact pool, and those match the oracle."""
+    from paged_kv_attention_28_amd import binding as B
+    lens, cached = ([300, 1000, 37, 2100], [299, 999, 36, 2099]) if kind == "decode" else \
+        ([300, 1000, 37, 700], [10, 511, 0, 256])
+    w1 = custom(lens, cached, kind=kind, seed=21, extra_blocks=2)
+    w2 = custom(lens, cached, kind=kind, seed=21, extra_blocks=2)
+    rng = np.random.default_rng(5)
+    pi = np.concatenate([[BIG_POOL - 1], 8192 + rng.choice(BIG_POOL - 8193, w2.num_blocks - 1, replace=False)])
+    for b in w2.setup + [w2.store]:
+        for s in b.seqs:
+            s.block_table = [int(pi[x]) for x in s.block_table]
+    w2.num_blocks = BIG_POOL
+    print(f"[past 4 GiB] {kind}: {len(lens)} sequences, pool {BIG_POOL} blocks", flush=True)
+    dw1 = H.DeviceWorkload(w1).build()
+    p1 = w1.passes[0]
+    q, m1 = dw1.pass_inputs(p1)
+    out1 = dw1.run_pass(p1, q, m1)
+    kc, vc = O.build_caches(w1, device="cuda")
+    assert np.array_equal(_cache_bits(dw1.k_cache), kc)
+    assert_close(out1, O.run_pass(w1, p1, kc, vc, q=q), m1.host.cu_seqlens_q, f"compact {kind}")
+
+    dw2 = H.DeviceWorkload(w2).build()
+    p2 = w2.passes[0]
+    q2, m2 = dw2.pass_inputs(p2)
+    assert torch.equal(q2.view(torch.int16), q.view(torch.int16))
+    # every stored row sits at its moved block, bit for bit
+    moved = torch.from_numpy(pi.astype(np.int64)).cuda()
+    for c1, c2 in ((dw1.k_cache, dw2.k_cache), (dw1.v_cache, dw2.v_cache)):
+        assert torch.equal(c2[moved].view(torch.int16), c1.view(torch.int16))
+    out2 = dw2.run_pass(p2, q2, m2)
+    assert torch.equal(out2.view(torch.int16), out1.view(torch.int16)), f"{kind}: moved blocks change the output"
+    if kind == "prefill":
+        grid = dw2.run_pass(p2, q2, m2, plan=False)
+        assert torch.equal(grid.view(torch.int16), out1.view(torch.int16)), "full-grid launch differs"
+    else:
+        # the fused store + decode into the moved blocks, from the setup state
+        dw3 = H.DeviceWorkload(w2)
+        dw3.run_setup()
+        key, value = W.store_kv(w2, "cuda")
+        ws = H.decode_workspace(w2, q2.shape[0], m2.max_context_len)
+        out3 = torch.full_like(q2, float("nan"))
+        B.paged_attn_decode_store(out3, q2, key, value, dw3.store_slots(), dw3.k_cache, dw3.v_cache,
+                                  m2.block_tables, m2.context_lens, w2.scale, m2.max_context_len, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out3.view(torch.int16), out1.view(torch.int16)), "fused decode store differs"
+        for c2, c3 in ((dw2.k_cache, dw3.k_cache), (dw2.v_cache, dw3.v_cache)):
+            assert torch.equal(c3[moved].view(torch.int16), c2[moved].view(torch.int16))
+        del dw3
+    del dw1, dw2
+    torch.cuda.empty_cache()
+
+
 def test_causality_bit_identical():
     """Overwriting K/V of a sequence's later positions leaves earlier prefill
     rows bit-identical."""
