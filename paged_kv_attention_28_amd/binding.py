@@ -319,14 +319,21 @@ def _torch():
 
 
 def _stream(stream=None) -> int:
+    """Raw HIP stream handle: `stream`'s, else the current device's current
+    stream (read through torch's raw-handle getter where the build has it:
+    building a Stream object costs about 2.5 us of host time per call)."""
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return int(s.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(torch.cuda.current_device()))
+    return int(torch.cuda.current_stream().cuda_stream)
 
 
 def _dev(t, name, dtype, contiguous=True):
     torch = _torch()
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")

@@ -390,6 +390,30 @@ def test_empty_calls_are_noops():
     assert (dw.k_cache.view(torch.int16) == H.NAN_BF16).all()
 
 
+def test_binding_launches_on_current_stream():
+    """The binding's default stream is torch's current stream, also inside a
+    `torch.cuda.stream` context; a store issued there lands after the work
+    queued before it on that stream."""
+    from paged_kv_attention_28_amd import binding as B
+    assert B._stream() == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    w = custom([300], [0], seed=4)
+    dw = H.DeviceWorkload(w)
+    key, value = W.store_kv(w, "cuda")
+    slots = dw.store_slots()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        assert B._stream() == side.cuda_stream
+        dw.k_cache.fill_(0)
+        dw.v_cache.fill_(0)
+        B.kv_store(key, value, dw.k_cache, dw.v_cache, slots)
+    side.synchronize()
+    assert B._stream() == torch.cuda.current_stream().cuda_stream
+    rows = torch.from_numpy(slots.cpu().numpy().astype(np.int64)).cuda()
+    kflat = dw.k_cache.view(-1, w.num_kv_heads, w.head_dim)
+    assert torch.equal(kflat[rows].view(torch.int16), key.view(torch.int16))
+
+
 def test_decode_graphs_replay_matches_eager():
     """Decode-step graphs (store + decode per bucket) give the bits of the
     eager calls on the same static buffers, for batches that hit an exact
