@@ -166,10 +166,10 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * Results are deterministic: the split of the work depends only on the
  * context lengths, max_context_len and the device's CU count (one
  * work-group of four wavefronts per CU on 3/4 of the CUs when
- * max_context_len <= 4096, else 7/8; at least 8 two-token steps per
+ * max_context_len <= 4096, else 7/8; at least 4 two-token steps per
  * wavefront), and partial results are combined in a fixed order that
- * depends on num_seqs (up to 32 sequences: up to four interleaved classes
- * of pieces per sequence, combined last; no atomics).
+ * depends on num_seqs (up to 32 sequences: 64 interleaved classes of pieces
+ * per sequence and head, combined in a fixed tree; no atomics).
  */
 pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, int32_t block_table_stride,

@@ -53,11 +53,8 @@ namespace {
 
 constexpr float kNegBig = -1e30f;  // running-max start: finite, so m - m_new never forms inf - inf
 constexpr int kWavesCap = 4096;    // persistent grid cap (partial slots are sized for it)
-constexpr int kMinStepsPerWave = 8;
-// Merge work-group: 16 lanes per query head, times the number of piece classes
-// (pieces i, i + SPLIT, ... are combined by one class; the classes meet in LDS).
-constexpr int kMergeSplit(int hq) { return hq * 16 * 4 <= 1024 ? 4 : 1024 / (hq * 16); }
-constexpr int kSplitMergeMaxSeqs = 32;  // batches up to this size use the split merge
+constexpr int kMinStepsPerWave = 4;
+constexpr int kWideMergeMaxSeqs = 32;  // batches up to this size merge per (sequence, head)
 constexpr int kMaxSeqs = 8192;     // LDS scan capacity
 // LDS reserved per stream work-group: more than half a CU's 160 KiB, so each
 // CU holds one work-group (one wavefront per SIMD). On the 256-sequence
@@ -253,34 +250,28 @@ __device__ void scan_steps(int* pre, const int32_t* __restrict__ ctx, int S, int
   __syncthreads();
 }
 
-// One work-group per sequence, 16 lanes per query head (8 dims per lane) in
-// each of SPLIT piece classes: zeros for a padding row (context 0); for a
-// sequence split between wavefronts, an online log-sum-exp combination of its
-// pieces, class c taking pieces c, c + SPLIT, ... (4 or 8 loaded at once, the
-// next batch in flight), after which classes 1.. hand their (m, l, o) to
-// class 0 through LDS; nothing for a sequence written whole. Several classes
-// shorten the serial chain of a small batch, whose sequences are cut into
-// many pieces; a large batch has few pieces per sequence and uses one class.
+// One work-group per sequence, 16 lanes per query head (8 dims per lane):
+// zeros for a padding row (context 0); for a sequence split between
+// wavefronts, an online log-sum-exp combination of its pieces (partials of
+// up to 4 pieces are loaded at once); nothing for a sequence written whole.
 // Pieces are the wavefronts wf .. wf + npieces - 1; the first one's partial
 // is in slot 1 unless the sequence starts exactly at that wavefront's range.
-template <int HQ, int SPLIT>
-__global__ __launch_bounds__(HQ * 16 * SPLIT) void decode_merge_kernel(uint16_t* __restrict__ out,
+template <int HQ>
+__global__ __launch_bounds__(HQ * 16) void decode_merge_kernel(uint16_t* __restrict__ out,
                                                                const int32_t* __restrict__ header,
                                                                const float* __restrict__ part_ml,
                                                                const float* __restrict__ part_o,
                                                                const int32_t* __restrict__ context_lens) {
   const int b = blockIdx.x;
-  const int sub = threadIdx.x / (HQ * 16);  // this thread combines pieces sub, sub + SPLIT, ...
-  const int t = threadIdx.x % (HQ * 16);
-  const int h = t >> 4;
-  const int d0 = 8 * (t & 15);
+  const int h = threadIdx.x >> 4;
+  const int d0 = 8 * (threadIdx.x & 15);
   const int L = context_lens[b];
   const int P = header[0];
   const int pb = header[1 + b];
   const int nb = header[2 + b] - pb;
   u32x4* op = reinterpret_cast<u32x4*>(out + ((int64_t)b * HQ + h) * kHeadDim + d0);
   if (L <= 0 || nb <= 0) {
-    if (sub == 0) *op = u32x4{0, 0, 0, 0};
+    *op = u32x4{0, 0, 0, 0};
     return;
   }
   const int wf = pb / P;
@@ -290,8 +281,7 @@ __global__ __launch_bounds__(HQ * 16 * SPLIT) void decode_merge_kernel(uint16_t*
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // pieces in batches of 8; the next batch is loaded before the current one
   // is combined, so only the first batch's latency is exposed
-  constexpr int kBatch = HQ * 16 * SPLIT > 512 ? 4 : 8;  // 1024-thread groups have half the registers
-  const int nsub = (npieces - sub + SPLIT - 1) / SPLIT;  // pieces of this class
+  constexpr int kBatch = HQ >= 64 ? 4 : 8;  // 1024-thread groups have half the registers
   struct Piece {
     float m[kBatch], l[kBatch];
     f32x4 lo[kBatch], hi[kBatch];
@@ -299,7 +289,7 @@ __global__ __launch_bounds__(HQ * 16 * SPLIT) void decode_merge_kernel(uint16_t*
   auto load = [&](Piece& pc, int i0) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int i = sub + SPLIT * (i0 + k < nsub ? i0 + k : nsub - 1);
+      const int i = i0 + k < npieces ? i0 + k : npieces - 1;
       const int w = wf + i;
       const int slot = (i == 0 && pb != w * P) ? 1 : 0;
       const int64_t pidx = ((int64_t)w * 2 + slot) * HQ + h;
@@ -312,7 +302,7 @@ __global__ __launch_bounds__(HQ * 16 * SPLIT) void decode_merge_kernel(uint16_t*
   auto combine = [&](const Piece& pc, int i0) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      if (i0 + k >= nsub) break;
+      if (i0 + k >= npieces) break;
       const float mn = fmaxf(M, pc.m[k]);
       const float fa = __builtin_amdgcn_exp2f(M - mn);
       const float fb = __builtin_amdgcn_exp2f(pc.m[k] - mn);
@@ -328,38 +318,133 @@ __global__ __launch_bounds__(HQ * 16 * SPLIT) void decode_merge_kernel(uint16_t*
       M = mn;
     }
   };
+  Piece cur, nxt;
+  load(cur, 0);
+  for (int i0 = 0; i0 < npieces; i0 += kBatch) {
+    const bool more = i0 + kBatch < npieces;
+    if (more) load(nxt, i0 + kBatch);
+    combine(cur, i0);
+    if (more) cur = nxt;
+  }
+  const float inv = 1.f / lsum;
+  *op = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+              pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
+}
+
+// Small-batch merge: one work-group per (sequence, query head), 64 piece
+// classes of 16 lanes (8 dims per lane); class c combines pieces c, c + 64,
+// ... (4 loaded at once, the next 4 in flight), so a sequence of up to 64
+// pieces costs one round of loads. The classes then meet in two stages: the
+// four classes of a wavefront by lane exchanges (lane ^ 16, lane ^ 32), the
+// sixteen wavefronts through LDS, where wavefront 0 combines four entries per
+// lane group and exchanges once more. Zeros for a padding row.
+template <int HQ>
+__global__ __launch_bounds__(1024) void decode_merge_wide_kernel(uint16_t* __restrict__ out,
+                                                                 const int32_t* __restrict__ header,
+                                                                 const float* __restrict__ part_ml,
+                                                                 const float* __restrict__ part_o,
+                                                                 const int32_t* __restrict__ context_lens) {
+  constexpr int kClasses = 64;
+  constexpr int kBatch = 4;
+  const int b = blockIdx.x;
+  const int h = blockIdx.y;
+  const int c = threadIdx.x >> 4;
+  const int d0 = 8 * (threadIdx.x & 15);
+  const int L = context_lens[b];
+  const int P = header[0];
+  const int pb = header[1 + b];
+  const int nb = header[2 + b] - pb;
+  u32x4* op = reinterpret_cast<u32x4*>(out + ((int64_t)b * HQ + h) * kHeadDim + d0);
+  if (L <= 0 || nb <= 0) {
+    if (c == 0) *op = u32x4{0, 0, 0, 0};
+    return;
+  }
+  const int wf = pb / P;
+  const int npieces = (pb + nb - 1) / P - wf + 1;
+  if (npieces == 1) return;
+  const int nsub = (npieces - c + kClasses - 1) / kClasses;
+  float M = kNegBig, lsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto comb = [&](float m2, float l2, const float (&a2)[8]) {
+    const float mn = fmaxf(M, m2);
+    const float fa = __builtin_amdgcn_exp2f(M - mn);
+    const float fb = __builtin_amdgcn_exp2f(m2 - mn);
+    lsum = lsum * fa + l2 * fb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] * fa + a2[e] * fb;
+    M = mn;
+  };
+  struct Piece {
+    float m[kBatch], l[kBatch];
+    f32x4 lo[kBatch], hi[kBatch];
+  };
+  auto load = [&](Piece& pc, int j0) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = c + kClasses * (j0 + k < nsub ? j0 + k : nsub - 1);
+      const int w = wf + i;
+      const int slot = (i == 0 && pb != w * P) ? 1 : 0;
+      const int64_t pidx = ((int64_t)w * 2 + slot) * HQ + h;
+      pc.m[k] = part_ml[pidx * 2];
+      pc.l[k] = part_ml[pidx * 2 + 1];
+      pc.lo[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0);
+      pc.hi[k] = *reinterpret_cast<const f32x4*>(part_o + pidx * kHeadDim + d0 + 4);
+    }
+  };
   if (nsub > 0) {
     Piece cur, nxt;
     load(cur, 0);
-    for (int i0 = 0; i0 < nsub; i0 += kBatch) {
-      const bool more = i0 + kBatch < nsub;
-      if (more) load(nxt, i0 + kBatch);
-      combine(cur, i0);
+    for (int j0 = 0; j0 < nsub; j0 += kBatch) {
+      const bool more = j0 + kBatch < nsub;
+      if (more) load(nxt, j0 + kBatch);
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (j0 + k >= nsub) break;
+        const float a2[8] = {cur.lo[k].x, cur.lo[k].y, cur.lo[k].z, cur.lo[k].w,
+                             cur.hi[k].x, cur.hi[k].y, cur.hi[k].z, cur.hi[k].w};
+        comb(cur.m[k], cur.l[k], a2);
+      }
       if (more) cur = nxt;
     }
   }
-  if constexpr (SPLIT > 1) {  // classes 1.. hand (m, l, o) to class 0 through LDS
-    __shared__ float red[SPLIT - 1][10][HQ * 16];
-    if (sub > 0) {
-      red[sub - 1][0][t] = M;
-      red[sub - 1][1][t] = lsum;
+  auto exchange = [&]() {  // combine with lanes ^ 16 and ^ 32 (the other classes of this wavefront)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[sub - 1][2 + e][t] = acc[e];
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float m2 = __shfl_xor(M, off);
+      const float l2 = __shfl_xor(lsum, off);
+      float a2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a2[e] = __shfl_xor(acc[e], off);
+      comb(m2, l2, a2);
     }
-    __syncthreads();
-    if (sub > 0) return;
+  };
+  exchange();
+  __shared__ float red[16][10][16];
+  const int wv = threadIdx.x >> 6;
+  const int ln = threadIdx.x & 63;
+  if (ln < 16) {
+    red[wv][0][ln] = M;
+    red[wv][1][ln] = lsum;
 #pragma unroll
-    for (int c = 0; c < SPLIT - 1; ++c) {
-      const float m2 = red[c][0][t];
-      const float mn = fmaxf(M, m2);
-      const float fa = __builtin_amdgcn_exp2f(M - mn);
-      const float fb = __builtin_amdgcn_exp2f(m2 - mn);
-      lsum = lsum * fa + red[c][1][t] * fb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * fa + red[c][2 + e][t] * fb;
-      M = mn;
-    }
+    for (int e = 0; e < 8; ++e) red[wv][2 + e][ln] = acc[e];
   }
+  __syncthreads();
+  if (wv != 0) return;
+  M = kNegBig;
+  lsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  const int g = ln >> 4, t = ln & 15;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int src = g + 4 * k;
+    float a2[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a2[e] = red[src][2 + e][t];
+    comb(red[src][0][t], red[src][1][t], a2);
+  }
+  exchange();
+  if (ln >= 16) return;
   const float inv = 1.f / lsum;
   *op = u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
               pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)};
@@ -762,11 +847,11 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   switch (num_q_heads) {  // HQ = G * H_kv, both powers of two up to 8
 #define PKV_MERGE(HQV)                                                                                  \
   case HQV:                                                                                             \
-    if (num_seqs <= kSplitMergeMaxSeqs)                                                                 \
-      hipLaunchKernelGGL((decode_merge_kernel<HQV, kMergeSplit(HQV)>), dim3(num_seqs),                  \
-                         dim3(HQV * 16 * kMergeSplit(HQV)), 0, s, o, header, part_ml, part_o, context_lens); \
+    if (num_seqs <= kWideMergeMaxSeqs)                                                                  \
+      hipLaunchKernelGGL((decode_merge_wide_kernel<HQV>), dim3(num_seqs, HQV), dim3(1024), 0, s, o, header, \
+                         part_ml, part_o, context_lens);                                               \
     else                                                                                                \
-      hipLaunchKernelGGL((decode_merge_kernel<HQV, 1>), dim3(num_seqs), dim3(HQV * 16), 0, s, o, header,  \
+      hipLaunchKernelGGL((decode_merge_kernel<HQV>), dim3(num_seqs), dim3(HQV * 16), 0, s, o, header,     \
                          part_ml, part_o, context_lens);                                                \
     break;
     PKV_MERGE(1) PKV_MERGE(2) PKV_MERGE(4) PKV_MERGE(8) PKV_MERGE(16) PKV_MERGE(32) PKV_MERGE(64)
