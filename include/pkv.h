@@ -358,10 +358,12 @@ int32_t pkv_sched_free_blocks(const pkv_sched* s);
  * replayed; at run time the smallest bucket holding the batch is chosen,
  * the inputs are copied into the static buffers and the padding rows get
  * slot -1 (P1, "其余部分": small-model decode is launch-bound, which is what
- * graphs remove). Each graph holds kv_store and paged_attn_decode (split
- * pass and merge) on rows [0, bucket) of the buffers below, exactly as the
- * eager calls would run them; a replay gives the same bits as those calls on
- * the same buffer contents.
+ * graphs remove). Each graph holds paged_attn_decode_store (the step's
+ * store fused into the split pass, then the merge) on rows [0, bucket) of
+ * the buffers below, exactly as the eager call would run it; a replay gives
+ * the bits of that call, which are those of kv_store followed by
+ * paged_attn_decode, on the same buffer contents. As for that call, the slot
+ * of row b is the cache row of position context_lens[b] - 1.
  *
  * All buffers are caller-owned device memory that must outlive the handle;
  * their contents at creation do not matter (creation only captures, it runs

@@ -1,5 +1,6 @@
 // Decode-step graphs: one HIP graph per batch bucket, each holding the step's
-// KV store and paged decode attention (split pass + merge) on static buffers.
+// KV store fused into paged decode attention (split pass + merge) on static
+// buffers: two kernels per step.
 //
 // P1 = "13. 读一个最小推理引擎：nano-vllm", "第五站：执行准备与 KV 容量" (CUDA
 // Graph paragraph): decode only, one graph per bucket (1, 2, 4, 8, then
@@ -37,12 +38,10 @@ namespace {
 
 // the decode step on the first `rows` rows of the static buffers
 pkv_status enqueue_step(const pkv_decode_graph_desc& d, int32_t rows, hipStream_t s) {
-  pkv_status st = kv_store(d.key, d.key_stride, d.value, d.value_stride, d.k_cache, d.v_cache, d.slot_mapping, rows,
-                           d.num_kv_heads, d.head_dim, d.block_size, d.num_blocks, s);
-  if (st != PKV_OK) return st;
-  return paged_attn_decode(d.out, d.q, d.k_cache, d.v_cache, d.block_tables, d.block_table_stride, d.context_lens,
-                           rows, d.num_q_heads, d.num_kv_heads, d.head_dim, d.block_size, d.num_blocks, d.scale,
-                           d.max_context_len, d.workspace, d.workspace_bytes, s);
+  return paged_attn_decode_store(d.out, d.q, d.key, d.key_stride, d.value, d.value_stride, d.slot_mapping, d.k_cache,
+                                 d.v_cache, d.block_tables, d.block_table_stride, d.context_lens, rows, d.num_q_heads,
+                                 d.num_kv_heads, d.head_dim, d.block_size, d.num_blocks, d.scale, d.max_context_len,
+                                 d.workspace, d.workspace_bytes, s);
 }
 
 }  // namespace

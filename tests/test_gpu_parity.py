@@ -415,8 +415,8 @@ def test_binding_launches_on_current_stream():
 
 
 def test_decode_graphs_replay_matches_eager():
-    """Decode-step graphs (store + decode per bucket) give the bits of the
-    eager calls on the same static buffers, for batches that hit an exact
+    """Decode-step graphs (the fused store + decode per bucket) give the bits
+    of the eager kv_store and paged_attn_decode calls on the same static buffers, for batches that hit an exact
     bucket and batches that need padding rows; each graph is replayed three
     times with unrelated eager work and synchronisation in between, and the
     real rows are also checked against the oracle."""
