@@ -202,6 +202,14 @@ EDGE = {
     "prefill_gqa4": dict(lens=[200, 333], cached=[0, 300], hq=32, hkv=8),
     "prefill_gqa8": dict(lens=[150, 40], cached=[3, 0], hq=16, hkv=2),
     "prefill_long_prefix": dict(lens=[2000, 1030], cached=[1999 - 700, 1024]),
+    # 64 query heads (8 per KV head): the widest merge work-groups, small batch and above 32 sequences
+    "decode_hq64": dict(lens=[3, 900, 2050], cached=[2, 899, 2049], hq=64, hkv=8, kind="decode"),
+    "decode_hq64_40seqs": dict(lens=[(37 * i) % 700 + 1 for i in range(40)],
+                               cached=[(37 * i) % 700 for i in range(40)], hq=64, hkv=8, kind="decode"),
+    # a single KV head: each load window spans 8 tokens of that head
+    "decode_hkv1": dict(lens=[1, 300, 1500], cached=[0, 299, 1499], hq=4, hkv=1, kind="decode"),
+    "prefill_hkv1": dict(lens=[150, 333], cached=[0, 200], hq=8, hkv=1),
+    "prefill_hq64": dict(lens=[100, 70], cached=[30, 0], hq=64, hkv=8),
 }
 
 
@@ -230,7 +238,8 @@ def test_edge_parity(name):
         assert (_f64(out[2:]) == 0).all()
 
 
-FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8"]
+FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
+               "decode_hq64", "decode_hq64_40seqs"]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES)
