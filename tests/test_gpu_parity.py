@@ -210,6 +210,9 @@ EDGE = {
     "decode_hkv1": dict(lens=[1, 300, 1500], cached=[0, 299, 1499], hq=4, hkv=1, kind="decode"),
     "prefill_hkv1": dict(lens=[150, 333], cached=[0, 200], hq=8, hkv=1),
     "prefill_hq64": dict(lens=[100, 70], cached=[30, 0], hq=64, hkv=8),
+    # contexts past 128 blocks (32768 tokens): block ids beyond those a wavefront keeps in registers
+    "decode_long_ctx": dict(lens=[40000, 5, 33000], cached=[39999, 4, 32999], kind="decode"),
+    "prefill_long_ctx": dict(lens=[33000, 300], cached=[32900, 0]),
 }
 
 
@@ -239,7 +242,7 @@ def test_edge_parity(name):
 
 
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
-               "decode_hq64", "decode_hq64_40seqs"]
+               "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx"]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES)
