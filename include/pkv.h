@@ -162,7 +162,9 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  *                    aligned), owned by the caller, reusable across calls on
  *                    one stream
  * Supported: head_dim 128, block_size 256, num_kv_heads in {1, 2, 4, 8},
- * num_q_heads / num_kv_heads in {1, 2, 4, 8}, num_seqs <= 8192.
+ * num_q_heads / num_kv_heads in {1, 2, 4, 8}, num_seqs <= 8192, and
+ * num_seqs * ceil(max_context_len / 2) <= 2^31 - 1 (else
+ * PKV_ERR_UNSUPPORTED).
  * Results are deterministic: the split of the work depends only on the
  * context lengths, max_context_len and the device's CU count (one
  * work-group of four wavefronts per CU on 3/4 of the CUs when

@@ -799,6 +799,9 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   if (block_table_stride < need_bt)
     return fail(PKV_ERR_INVALID, "paged_attn_decode: block_table_stride %d < %lld blocks of max_context_len",
                 block_table_stride, (long long)need_bt);
+  // the kernels count two-token steps (a step holds at least two tokens) in 32-bit integers
+  if ((int64_t)num_seqs * ((max_context_len + 1) / 2) > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: num_seqs x max_context_len / 2 exceeds 2^31 - 1 steps");
   const size_t ws = paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len);
   if (!workspace || workspace_bytes < ws)
     return fail(PKV_ERR_WORKSPACE, "paged_attn_decode: workspace of %zu bytes needed, got %zu", ws, workspace_bytes);

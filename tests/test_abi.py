@@ -151,6 +151,9 @@ def test_decode_validation(lib):
     assert lib.paged_attn_decode(*args(bts=4)) == 1          # stride < 2048 / 256
     assert lib.paged_attn_decode(*args(wsb=16)) == 4         # workspace too small
     assert lib.paged_attn_decode(*args(ws=F + 16)) == 2      # workspace misaligned
+    # 8192 sequences x 2^20 tokens: more two-token steps than a 32-bit count holds
+    assert lib.paged_attn_decode(*args(S=8192, maxctx=1 << 20, bts=4096)) == 2
+    assert "steps" in P.last_error()
     assert lib.paged_attn_decode(*args(S=0)) == 0
 
 
