@@ -18,7 +18,10 @@ budget) in TFLOP/s of unmasked attention flops against the 2.5 PFLOP/s bf16
 MFMA peak, its roofline fraction max(t_MFMA, t_HBM) / t (HBM bytes: q, out and
 the distinct context K/V rows), and the same call launched back to back for
 0.1 s (the shader clock under this load depends on how busy the GPU is kept).
-``hbm_copy_ceiling`` is torch's own copy over 2 GiB. ``trace_replay`` replays
+``long_decode`` times the decode step of the long-context workload (512
+sequences, contexts U[4096, 32768], 32 Q / 8 KV heads, about 38.7 GB of K/V
+per call) against the HBM peak. ``hbm_copy_ceiling`` is torch's own copy over
+2 GiB. ``trace_replay`` replays
 the 28-layer scheduler trace (256 requests) and reports decode GB/s, prefill
 TFLOP/s and kernel-only tokens/s from events around each layer's kernels. ``cpu_baseline`` times the
 fp64 oracle on the same decode step on the host (about 10 s of repeats)
@@ -26,6 +29,7 @@ before the GPU is initialised.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-prefill] [--no-graph] [--no-back-to-back] [--no-trace] [--no-fused]
+                       [--no-long]
 """
 
 from __future__ import annotations
@@ -393,6 +397,36 @@ def sampler_rate(torch, dev, reps: int = 20):
             "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)}
 
 
+def long_decode(torch, dev, steps: int, warmup: int) -> dict:
+    """Long-context decode: 512 sequences with contexts U[4096, 32768], 32 Q / 8 KV heads, a fully shuffled pool.
+    The same decode step as the headline workload (host preparation, upload, kv_store, paged_attn_decode), timed
+    over a few steps; each call reads about 38.7 GB of K/V."""
+    from paged_kv_attention_28_amd import harness as H
+    w = W.make(4)
+    log("[bench] long-context decode: setup stores (about 77 GB of K/V) ...")
+    dw = H.DeviceWorkload(w, dev)
+    dw.run_setup()
+    torch.cuda.synchronize()
+    runner = H.StepRunner(dw, w.passes[0])
+    ms, store_ms, attn_ms = time_steps(runner, steps, warmup, torch)
+    db = decode_bytes(w)
+    attn = float(attn_ms.mean())
+    gbs = db["attn"] / (attn * 1e-3) / 1e9
+    log(f"[bench] long-context decode: attention {attn:.3f} ms -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM "
+        f"peak); step {ms:.3f} ms wall")
+    seqs = w.passes[0].batch.seqs
+    out = {"workload": f"long-context decode: {len(seqs)} seqs, context U[4096, 32768] "
+                       f"(max {max(s.seq_len for s in seqs)}), GQA {w.num_q_heads}Q/{w.num_kv_heads}KV, head_dim "
+                       f"{w.head_dim}, bf16, block 256, fully shuffled pool; step = host prepare + upload + kv_store "
+                       f"+ paged_attn_decode",
+           "steps": steps, "attn_ms": round(attn, 4), "gbs": round(gbs, 1),
+           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": db["attn"],
+           "ms_per_step": round(ms, 4)}
+    del runner, dw
+    torch.cuda.empty_cache()
+    return out
+
+
 def graph_vs_eager(torch, dev, iters: int = 200):
     """Host-side cost of a decode step (store + attention) issued eagerly
     through the binding versus replayed from a captured graph, on decode
@@ -466,6 +500,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the 28-layer scheduler-trace replay")
     ap.add_argument("--no-fused", action="store_true", help="skip the decode step with the store fused")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context decode (512 seqs, 4K-32K tokens)")
     ap.add_argument("--no-back-to-back", action="store_true",
                     help="skip the 0.1 s back-to-back prefill run (keeps a kernel trace to the timed steps)")
     args = ap.parse_args()
@@ -554,6 +589,7 @@ def main():
                    "back_to_back": b2b_line,
                    "rope_kv_store": rope}
 
+    long_dec = None if args.no_long else long_decode(torch, dev, max(args.steps // 5, 5), 3)
     graph = None if args.no_graph else graph_vs_eager(torch, dev)
     sampler = sampler_rate(torch, dev)
     trace = None if args.no_trace else trace_replay(torch)
@@ -585,6 +621,7 @@ def main():
         "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
         "decode_step_fused": fused,
         "prefill": prefill,
+        "long_decode": long_dec,
         "decode_graph": graph,
         "sampler": sampler,
         "trace_replay": trace,
