@@ -816,11 +816,12 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = stream_lds(num_seqs);
   // Part of the CUs, by the caller's bound on the context: measured on MI355X (256 CUs) over 128..256
-  // work-groups, contexts up to 2048 ran fastest on 176-192 (192 against 256: 5.6 % on 256 sequences, 6 % on
-  // 64) and contexts of 4096-32768 on 224 (2.5 % against 256; 192 was 10 % slower there).
+  // work-groups, contexts up to 2048 ran fastest on 192 (against 256: 5.6 % on 256 sequences, 6 % on 64;
+  // 64..256 sequences all best at 192), contexts of 4096-32768 on all 256 (5 % against 224, 128 and 512
+  // sequences, two machines).
   const int resident = resident_wgs(pick_kernel(G, num_kv_heads), lds);
   if (resident <= 0) return fail(PKV_ERR_HIP, "paged_attn_decode: cannot query the device");
-  const int grid = resident < 8 ? resident : (max_context_len <= 4096 ? resident * 3 / 4 : resident * 7 / 8);
+  const int grid = resident < 8 || max_context_len > 4096 ? resident : resident * 3 / 4;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
