@@ -167,8 +167,8 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * PKV_ERR_UNSUPPORTED).
  * Results are deterministic: the split of the work depends only on the
  * context lengths, max_context_len and the device's CU count (one
- * work-group of four wavefronts per CU on 3/4 of the CUs when
- * max_context_len <= 4096, else on all; at least 4 two-token steps per
+ * work-group of four wavefronts per CU, on 3/4 of the CUs for one or two
+ * query heads per KV head, else on all; at least 4 two-token steps per
  * wavefront), and partial results are combined in a fixed order that
  * depends on num_seqs (up to 32 sequences: 64 interleaved classes of pieces
  * per sequence and head, combined in a fixed tree; no atomics).

@@ -815,13 +815,13 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   float* part_o = reinterpret_cast<float*>(wsb + lo.header_bytes + lo.ml_bytes);
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = stream_lds(num_seqs);
-  // Part of the CUs, by the caller's bound on the context: measured on MI355X (256 CUs) over 128..256
-  // work-groups, contexts up to 2048 ran fastest on 192 (against 256: 5.6 % on 256 sequences, 6 % on 64;
-  // 64..256 sequences all best at 192), contexts of 4096-32768 on all 256 (5 % against 224, 128 and 512
-  // sequences, two machines).
+  // Part of the CUs, by the query heads per KV head: measured on MI355X (256 CUs) with 192, 224 and 256
+  // work-groups, one or two query heads per KV head (a step's arithmetic is light) ran fastest on 192 at
+  // every context length tried (U[100, 2048] to U[4096, 32768]; 2-6 % ahead of 256), four or eight (twice
+  // to four times the arithmetic per byte) on all 256 (5-15 % ahead of 192 at four, 20-25 % at eight).
   const int resident = resident_wgs(pick_kernel(G, num_kv_heads), lds);
   if (resident <= 0) return fail(PKV_ERR_HIP, "paged_attn_decode: cannot query the device");
-  const int grid = resident < 8 || max_context_len > 4096 ? resident : resident * 3 / 4;
+  const int grid = resident < 8 || G >= 4 ? resident : resident * 3 / 4;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
