@@ -205,16 +205,41 @@ __device__ __forceinline__ void compute_buf(State<G>& S, const Buf& x, const u32
       vf[t][8 * half + 7] = bf_hi(w.w);
     }
   }
+  if constexpr (G >= 8) {
+    // Lazy rescale (eight query heads per KV head, where a step's arithmetic is the bound): a head's reference
+    // max moves only when a score exceeds it by more than 8 (log2 units), so the weights stay <= 2^8 and the 16
+    // output multiplies are skipped whenever no lane of the wavefront moves. With fewer heads per KV head the
+    // stream is memory-bound and this measured no faster (G = 4: -2 % to +4 %), so they keep the eager form.
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mn = fmaxf(S.m[h], fmaxf(sc[0][h], sc[1][h]));
-    const float alpha = __builtin_amdgcn_exp2f(S.m[h] - mn);
-    const float p0 = __builtin_amdgcn_exp2f(sc[0][h] - mn);
-    const float p1 = __builtin_amdgcn_exp2f(sc[1][h] - mn);
-    S.l[h] = S.l[h] * alpha + (p0 + p1);
+    for (int h = 0; h < G; ++h) {
+      const float mx = fmaxf(sc[0][h], sc[1][h]);
+      const bool grow = mx > S.m[h] + 8.f;
+      const float mn = grow ? mx : S.m[h];
+      const float p0 = __builtin_amdgcn_exp2f(sc[0][h] - mn);
+      const float p1 = __builtin_amdgcn_exp2f(sc[1][h] - mn);
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float alpha = __builtin_amdgcn_exp2f(S.m[h] - mn);
+        S.l[h] *= alpha;
 #pragma unroll
-    for (int d = 0; d < 16; ++d) S.o[h][d] = S.o[h][d] * alpha + p0 * vf[0][d] + p1 * vf[1][d];
-    S.m[h] = mn;
+        for (int d = 0; d < 16; ++d) S.o[h][d] *= alpha;
+      }
+      S.l[h] += p0 + p1;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) S.o[h][d] = S.o[h][d] + p0 * vf[0][d] + p1 * vf[1][d];
+      S.m[h] = mn;
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mn = fmaxf(S.m[h], fmaxf(sc[0][h], sc[1][h]));
+      const float alpha = __builtin_amdgcn_exp2f(S.m[h] - mn);
+      const float p0 = __builtin_amdgcn_exp2f(sc[0][h] - mn);
+      const float p1 = __builtin_amdgcn_exp2f(sc[1][h] - mn);
+      S.l[h] = S.l[h] * alpha + (p0 + p1);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) S.o[h][d] = S.o[h][d] * alpha + p0 * vf[0][d] + p1 * vf[1][d];
+      S.m[h] = mn;
+    }
   }
 }
 
