@@ -277,6 +277,26 @@ def test_decode_store_fused_matches_two_calls(case):
     assert np.array_equal(_cache_bits(dw.v_cache), va), f"{case}: V cache differs"
 
 
+def test_prefill_long_prompt_sampled():
+    """One 16384-token prompt (the whole token budget in one sequence: 256 query tiles, 64 blocks), launched on
+    the plan and on the full grid: sampled rows against the oracle, each row computed by the oracle's decode
+    over that row's causal context (decode = last prefill row is a pinned oracle identity)."""
+    from oracle import paged as op
+    w = custom([16384], [0], seed=17)
+    dw = H.DeviceWorkload(w).build()
+    p = w.passes[0]
+    q, m = dw.pass_inputs(p)
+    out = dw.run_pass(p, q, m)
+    grid = dw.run_pass(p, q, m, plan=False)
+    assert torch.equal(grid.view(torch.int16), out.view(torch.int16)), "plan and grid launches differ"
+    kc, vc = O.build_caches(w, device="cuda")
+    rows = np.array([0, 1, 63, 64, 127, 128, 1000, 4095, 4096, 8191, 12000, 16382, 16383])
+    sel = torch.from_numpy(rows).cuda()
+    bt = np.asarray(w.store.seqs[0].block_table, dtype=np.int32)[None, :].repeat(len(rows), 0)
+    ref = op.decode_ref(O.bits(q[sel]), kc, vc, bt, (rows + 1).astype(np.int32), w.scale)
+    assert_close(out[sel], ref, None, "16384-token prompt, sampled rows")
+
+
 def test_prefill_first_row_exact():
     """Row 0 of an uncached prompt sees only key 0: output = V row 0 exactly."""
     w = custom([70, 300], [0, 0], seed=3)
