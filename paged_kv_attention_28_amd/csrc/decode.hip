@@ -22,9 +22,11 @@
 //    divided evenly over all wavefronts of a persistent grid, so
 //    there are no empty work-groups and no tail of unequal splits. The grid
 //    is one work-group per CU (the launch reserves enough LDS for that), i.e.
-//    one wavefront per SIMD, on 3/4 of the CUs for contexts up to 4096 and
-//    7/8 beyond: fewer, longer ranges than the two per SIMD the registers
-//    would allow, which streams faster. A
+//    one wavefront per SIMD, on 3/4 of the CUs for one or two query heads per
+//    KV head and on all CUs for four or eight (their heavier arithmetic gains
+//    from every CU): fewer, longer ranges than the two per SIMD the registers
+//    would allow, which streams faster; each wavefront takes at least 4 steps.
+//    A
 //    wavefront walks its range across sequence boundaries with the loads of
 //    the next step always in flight (two register buffers; block-table rows
 //    and the next sequence's queries are prefetched). K/V loads are
@@ -36,7 +38,9 @@
 //    work-group per sequence, all heads at once) finds the pieces from the
 //    same step arithmetic and combines them (log-sum-exp in the log2
 //    domain), loading them 8 at a time with the next 8 already in flight;
-//    it also writes zeros for padding rows (context 0). (Merging
+//    it also writes zeros for padding rows (context 0). Batches of up to 32
+//    sequences, whose sequences are cut into many pieces, use a wide merge
+//    (one work-group per sequence and head, 64 piece classes). (Merging
 //    inside the stream kernel would need a device-scope release per piece,
 //    which writes back the whole L2 of the XCD on this GPU.)
 //  * Positions past the context end load the last context row (always
