@@ -19,7 +19,10 @@ with theta = 1e6 by default. Every head (query and key) uses the same angles;
 values are not rotated. Pins (tests/test_rope.py): position 0 is the
 identity; each pair keeps its norm; rotations compose (positions add); the
 product of a rotated query and a rotated key depends only on the position
-difference; D = 2 is the plain 2-d rotation by pos radians.
+difference; D = 2 is the plain 2-d rotation by pos radians; unit vectors turn
+by angles worked out by hand for theta = 10^4, D = 8 (pair i at 10^-i rad per
+position) and for theta = 10^6, D = 128 (pairs 0 and 32), which pins the
+frequency schedule (tests/golden/rope_angles_closed_form.json).
 """
 
 from __future__ import annotations

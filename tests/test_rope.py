@@ -68,6 +68,27 @@ def test_two_dims_are_the_plane_rotation():
     np.testing.assert_allclose(y[:, 0, 1], s * x[:, 0, 0] + c * x[:, 0, 1], rtol=1e-14, atol=1e-15)
 
 
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "rope_angles_closed_form.json")
+
+
+def test_unit_vectors_turn_by_the_hand_worked_angles():
+    """Pins the frequency schedule: unit vectors along dim i rotate to (cos a_i, sin a_i) on dims (i, i + D/2),
+    with the angles a_i worked out by hand for theta = 10^4, D = 8 (pair i turns at 10^-i rad per position)
+    and for theta = 10^6, D = 128 (pairs 0 and 32), in tests/golden/rope_angles_closed_form.json."""
+    import json
+    cases = json.load(open(GOLDEN))["cases"]
+    for c in cases:
+        D = c["head_dim"]
+        pairs = c.get("pairs", list(range(D // 2)))
+        for i, a in zip(pairs, c["angles"]):
+            x = np.zeros((1, 1, D))
+            x[0, 0, i] = 1.0
+            y = orope.rope_ref(x, [c["pos"]], theta=c["theta"])[0, 0]
+            want = np.zeros(D)
+            want[i], want[i + D // 2] = np.cos(a), np.sin(a)
+            np.testing.assert_allclose(y, want, rtol=0, atol=1e-9, err_msg=f"D={D} pos={c['pos']} pair {i}")
+
+
 def test_bf16_rounding_matches_torch():
     x = np.concatenate([_rand(10000, 7) * 10, [0.0, -0.0, 1.0, 1.00390625, 1.01171875, -3.3e-39]])
     bits = orope.f64_to_bf16_bits(x)
@@ -96,24 +117,44 @@ def test_fused_store_reference():
     np.testing.assert_allclose(q_rot, orope.rope_ref(q, pos))
 
 
-@pytest.mark.parametrize("mutant", ["k_turns_backwards", "one_head_unrotated"])
+@pytest.mark.parametrize("mutant", ["k_turns_backwards", "one_head_unrotated", "exponent_i_over_d",
+                                    "pairs_interleaved"])
 def test_planted_mistakes_fail_a_pin(mutant, monkeypatch):
     real = orope.rope_ref
+    real_angles = orope.rope_angles
+    if mutant == "exponent_i_over_d":          # theta^(-i/D) instead of theta^(-2i/D)
+        def angles(positions, head_dim, theta=orope.DEFAULT_THETA):
+            i = np.arange(head_dim // 2, dtype=np.float64)
+            return np.asarray(positions, dtype=np.float64)[:, None] * (theta ** (-i / head_dim))[None, :]
+        monkeypatch.setattr(orope, "rope_angles", angles)
+    if mutant == "pairs_interleaved":          # pair (2i, 2i + 1) instead of (i, i + D/2)
+        def inter(x, positions, theta=orope.DEFAULT_THETA):
+            x = op.bf16_bits_to_f64(x) if np.asarray(x).dtype == np.uint16 else np.asarray(x, dtype=np.float64)
+            D = x.shape[-1]
+            a = real_angles(positions, D, theta)[:, None, :]
+            c, s = np.cos(a), np.sin(a)
+            y = x.copy()
+            y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+            y[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * s
+            return y
+        monkeypatch.setattr(orope, "rope_ref", inter)
 
     def bad(x, positions, theta=orope.DEFAULT_THETA, _k=[0]):
         y = real(x, positions, theta)
         _k[0] += 1
         if mutant == "k_turns_backwards" and _k[0] % 2 == 0:
             return real(x, -np.asarray(positions, dtype=np.float64), theta)
-        if mutant == "one_head_unrotated":
+        if mutant == "one_head_unrotated" and y.shape[1] > 1:
             y = y.copy()
             y[:, 1] = op.bf16_bits_to_f64(x)[:, 1] if np.asarray(x).dtype == np.uint16 else np.asarray(x)[:, 1]
         return y
 
-    monkeypatch.setattr(orope, "rope_ref", bad)
+    if mutant in ("k_turns_backwards", "one_head_unrotated"):
+        monkeypatch.setattr(orope, "rope_ref", bad)
     failed = 0
     for pin in (test_position_zero_is_identity, test_pairs_keep_their_norm, test_rotations_compose,
-                test_scores_depend_on_relative_position_only, test_every_head_turns_the_same_way):
+                test_scores_depend_on_relative_position_only, test_every_head_turns_the_same_way,
+                test_unit_vectors_turn_by_the_hand_worked_angles):
         try:
             pin()
         except AssertionError:
