@@ -35,8 +35,9 @@
 //    (ds_read_b64_tr_b16), so V is staged exactly like K.
 //  * fp32 online softmax in the log2 domain with lazy rescaling (the
 //    reference max moves only when a row max exceeds it by 8, so most tiles
-//    skip rescaling the 64 output accumulators); a wavefront skips the tiles
-//    above its last query row.
+//    skip rescaling the 64 output accumulators); the row sum adds the
+//    weights as rounded to bf16 for the P V products; a wavefront skips the
+//    tiles above its last query row.
 //  * K/V of tile i+1 go from the cache straight into LDS (buffer loads with
 //    the lds bit, buffer_load_dwordx4 ... lds: a scalar descriptor per tile
 //    and loop-invariant 32-bit lane offsets) while tile i is computed: no
@@ -101,6 +102,12 @@ template <int N>
 struct Stage {
   static constexpr int value = N;
 };
+
+// c + the two bf16 halves of w (v_dot2_f32_bf16 against 1.0, 1.0)
+__device__ __forceinline__ float dot2_ones(uint32_t w, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3F803F80u), c,
+                                         false);
+}
 
 // max of x over lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip)
 __device__ __forceinline__ float max_lane32(float x) {
@@ -350,16 +357,12 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
           for (int i = 0; i < 16; ++i) acc_o[dt][i] *= alpha;
         m_ref = m_new;
       }
-      float lsum = -0.f;  // -0 + x == x exactly, so the first add folds away
       u32x4 pk[kSub][2];
 #pragma unroll
       for (int st = 0; st < kSub; ++st) {
         float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][i], scale_log2, -m_ref));
-          lsum += p[i];
-        }
+        for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[st][i], scale_log2, -m_ref));
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
           pk[st][qq].x = pack_bf16x2(p[8 * qq + 0], p[8 * qq + 1]);
@@ -368,7 +371,21 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
           pk[st][qq].w = pack_bf16x2(p[8 * qq + 6], p[8 * qq + 7]);
         }
       }
-      l_run += lsum;
+      // Row sum of the weights as rounded to bf16 for the P V products, so
+      // the output is divided by exactly the weights that were applied: with
+      // the lazy reference max the largest weight lies anywhere in (1, 256]
+      // and its rounding would otherwise show in full in a peaky row's output.
+      float lsum0 = 0.f, lsum1 = 0.f;
+#pragma unroll
+      for (int st = 0; st < kSub; ++st)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          lsum0 = dot2_ones(pk[st][qq].x, lsum0);
+          lsum1 = dot2_ones(pk[st][qq].y, lsum1);
+          lsum0 = dot2_ones(pk[st][qq].z, lsum0);
+          lsum1 = dot2_ones(pk[st][qq].w, lsum1);
+        }
+      l_run += lsum0 + lsum1;
       // key chunk outer, output dims inner: the four products of the first 16
       // keys need only the first half of the weights, so the second half's
       // exponentials can run while they execute

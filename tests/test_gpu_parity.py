@@ -152,8 +152,14 @@ def test_long_decode_sampled():
     out = dw.run_pass(p, q, m)
     torch.cuda.synchronize()
     lens = np.asarray([s.seq_len for s in p.batch.seqs])
+    # 64 sequences: the 8 longest (cut into the most pieces between wavefronts), the 8 shortest and 48 drawn
+    order = np.argsort(lens, kind="stable")
+    ends = [int(x) for x in order[-8:]] + [int(x) for x in order[:8]]
+    rest = np.setdiff1d(np.arange(len(lens)), ends)
     rng = np.random.default_rng(44)
-    idx = sorted(set([int(lens.argmax()), int(lens.argmin())] + [int(x) for x in rng.choice(len(lens), 6, False)]))
+    idx = sorted(set(ends + [int(x) for x in rng.choice(rest, 48, replace=False)]))
+    assert len(idx) == 64
+    print(f"[long decode] checking {len(idx)} sequences, contexts {lens[idx].min()}..{lens[idx].max()}", flush=True)
     ref = O.decode_sampled(w, idx, device="cuda")
     assert_close(out[idx], ref, None, "config 4 sampled decode")
     # the store of the sampled sequences' rows is a bit copy of the generated values
@@ -175,9 +181,12 @@ def test_long_decode_sampled():
 # edge cases on small hand-built workloads
 # ----------------------------------------------------------------------------
 
-def custom(lens, cached, hq=16, hkv=8, kind="prefill", seed=7, pad=0, extra_blocks=4, kv_mod=None):
+def custom(lens, cached, hq=16, hkv=8, kind="prefill", seed=7, pad=0, extra_blocks=4, q_mult=1.0, q_bias=0.0,
+           k_ramp=0.0):
     """A workload with the given lengths / cached prefixes, a shuffled pool,
-    one setup store of every cached token and one step store."""
+    one setup store of every cached token and one step store. q_mult scales
+    the queries (peaky softmax); q_bias with k_ramp makes every query head's
+    scores rise along the context (the running max moves on every key tile)."""
     rng = np.random.default_rng(seed)
     nb = [-(-L // 256) for L in lens]
     pool = W._Pool(rng, sum(nb) + extra_blocks)
@@ -186,8 +195,19 @@ def custom(lens, cached, hq=16, hkv=8, kind="prefill", seed=7, pad=0, extra_bloc
     if not setup[0].seqs:
         setup = []
     step = W.Batch([W.Seq(L, c, t) for L, c, t in zip(lens, cached, tables)], num_pad=pad, stream=6)
-    return W.Workload("custom", seed, hq, hkv, 128, 256, sum(nb) + extra_blocks, max(nb), setup, step,
-                      [W.Pass(kind, step)])
+    w = W.Workload("custom", seed, hq, hkv, 128, 256, sum(nb) + extra_blocks, max(nb), setup, step,
+                   [W.Pass(kind, step)])
+    w.q_mult, w.q_bias, w.k_ramp = q_mult, q_bias, k_ramp
+    return w
+
+
+def _dec(lens, **kw):
+    """Decode case: every sequence's last token is the step's."""
+    return dict(lens=lens, cached=[L - 1 for L in lens], kind="decode", **kw)
+
+
+PEAKY = dict(q_mult=8.0)                 # scores ~8x wider: the max moves often and by a lot
+RAMP = dict(q_bias=1.0, k_ramp=0.03)     # scores rise ~15 log2 units per 32 keys along every context
 
 
 EDGE = {
@@ -213,6 +233,30 @@ EDGE = {
     # contexts past 128 blocks (32768 tokens): block ids beyond those a wavefront keeps in registers
     "decode_long_ctx": dict(lens=[40000, 5, 33000], cached=[39999, 4, 32999], kind="decode"),
     "prefill_long_ctx": dict(lens=[33000, 300], cached=[32900, 0]),
+    # softmax edge cases: peaky scores (q x 8) and scores rising along the context, for every
+    # rescaling form: eager (G <= 2, G = 4 up to 4096 tokens), lazy (G = 4 beyond 4096, G = 8, prefill)
+    "decode_peaky_gqa2": _dec([1, 97, 700, 2048, 3000], **PEAKY),
+    "decode_peaky_gqa4": _dec([5, 900, 3000], hq=32, **PEAKY),
+    "decode_peaky_gqa4_long": _dec([4097, 6000, 9001, 300, 12], hq=32, **PEAKY),
+    "decode_peaky_gqa8": _dec([3, 1200, 5000], hq=64, **PEAKY),
+    "decode_ramp_gqa2": _dec([2, 64, 777, 2048, 2900], **RAMP),
+    "decode_ramp_gqa4_long": _dec([4097, 5000, 7000, 33], hq=32, **RAMP),
+    "decode_ramp_gqa8": _dec([300, 2500, 4100], hq=16, hkv=2, **RAMP),
+    "decode_ramp_40seqs": _dec([(53 * i) % 1500 + 1 for i in range(40)], **RAMP),
+    "prefill_peaky": dict(lens=[300, 1000, 70, 600], cached=[0, 511, 0, 256], **PEAKY),
+    "prefill_peaky_gqa8": dict(lens=[333, 129], cached=[100, 0], hq=64, **PEAKY),
+    "prefill_ramp": dict(lens=[300, 1000, 70, 600], cached=[0, 511, 0, 256], **RAMP),
+    "prefill_ramp_gqa4": dict(lens=[700, 129], cached=[256, 0], hq=32, **RAMP),
+    "prefill_ramp_gqa1": dict(lens=[500], cached=[37], hq=8, **RAMP),
+    # four KV heads (the per-GPU shape of a two-way head split of 8 Q / 8 KV ... 16 Q / 8 KV layers)
+    "decode_hkv4_gqa2": _dec([1, 300, 1999, 2048], hq=8, hkv=4),
+    "decode_hkv4_gqa4": _dec([7, 256, 257, 3000], hq=16, hkv=4),
+    "decode_hkv4_gqa4_long": _dec([5000, 4097, 100], hq=16, hkv=4, **PEAKY),
+    "prefill_hkv4_gqa2": dict(lens=[300, 129, 1000], cached=[0, 100, 511], hq=8, hkv=4),
+    "prefill_hkv4_gqa4": dict(lens=[257, 700], cached=[0, 256], hq=16, hkv=4),
+    # more than 32 sequences with 8 and 4 query heads: the per-sequence (serial) merge
+    "decode_hq8_hkv4_40seqs": _dec([(41 * i) % 900 + 1 for i in range(40)], hq=8, hkv=4),
+    "decode_hq4_hkv1_40seqs": _dec([(29 * i) % 1300 + 1 for i in range(40)], hq=4, hkv=1),
 }
 
 
@@ -242,7 +286,8 @@ def test_edge_parity(name):
 
 
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
-               "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx"]
+               "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
+               "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs"]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES)
@@ -412,6 +457,35 @@ def test_causality_bit_identical():
     assert not torch.equal(a[cut + 1:].view(torch.int16), b[cut + 1:].view(torch.int16))
 
 
+@pytest.mark.parametrize("hkv", [1, 2, 3, 4, 5, 12, 16])
+def test_store_head_counts_bit_exact(hkv):
+    """kv_store for every chunks-per-lane form (1..4 sixteen-byte chunks per lane: up to 4, 8, 12 and 16
+    KV heads), with -1 rows interleaved and a token stride wider than a row: the whole pool bit-exact
+    against the oracle's store."""
+    import paged_kv_attention_28_amd as P
+    from oracle import paged as op
+    rng = np.random.default_rng(100 + hkv)
+    nblk, T = 6, 700
+    slots = rng.choice(nblk * 256, size=T, replace=False).astype(np.int32)
+    slots[rng.choice(T, size=40, replace=False)] = -1
+    stride = hkv * 128 + 64                              # token stride wider than a row (a fused-buffer view)
+    kbuf = W.randn_bf16(9, hkv, W.TAG_K, (T, stride), "cuda")
+    vbuf = W.randn_bf16(9, hkv, W.TAG_V, (T, stride), "cuda")
+    key = kbuf.as_strided((T, hkv, 128), (stride, 128, 1))
+    value = vbuf.as_strided((T, hkv, 128), (stride, 128, 1))
+    kc = torch.empty(nblk, 256, hkv, 128, dtype=torch.bfloat16, device="cuda")
+    kc.view(torch.int16).fill_(H.NAN_BF16)
+    vc = kc.clone()
+    P.kv_store(key, value, kc, vc, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    k0 = np.full((nblk, 256, hkv, 128), H.NAN_BF16, dtype=np.uint16)
+    kb = O.bits(kbuf)[:, :hkv * 128].reshape(T, hkv, 128)
+    vb = O.bits(vbuf)[:, :hkv * 128].reshape(T, hkv, 128)
+    kref, vref = op.kv_store_ref(k0, k0.copy(), kb, vb, slots)
+    assert np.array_equal(_cache_bits(kc), kref)
+    assert np.array_equal(_cache_bits(vc), vref)
+
+
 def test_empty_calls_are_noops():
     import paged_kv_attention_28_amd as P
     w = custom([10], [0])
@@ -515,7 +589,7 @@ def _within_one_bf16_unit(gpu, ref, what):
     assert not bad.any(), f"{what}: {bad.sum()} elements beyond one bf16 unit, worst {np.abs(gpu - ref).max():.3e}"
 
 
-@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 2)])
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 8), (8, 2), (8, 4), (16, 4)])
 def test_rope_kv_store_parity(hq, hkv):
     """Fused rotary + store against the oracle: rotated q (every row) and the
     stored rotated K rows within one bf16 unit of the fp64 rotation; V rows
@@ -589,7 +663,16 @@ def test_sampler_matches_oracle_decision(rows, vocab, pad):
     out = torch.full((rows,), -1, dtype=torch.int32, device="cuda")
     P.sample_temperature(out, dl, torch.from_numpy(temps).cuda(), dg)
     want = OSm.sample_decision(logits[:, :vocab], temps, g[:, :vocab])
-    assert np.array_equal(out.cpu().numpy(), want)
+    got = out.cpu().numpy()
+    assert np.array_equal(got, want)
+    # against the definition argmax softmax(l / T) / E (fp64, E = exp(-g)) wherever the two best fp64
+    # keys are further apart than fp32 rounding can blur
+    exact = OSm.sample_exact(logits[:, :vocab], temps, np.exp(-g[:, :vocab].astype(np.float64)))
+    keys = logits[:, :vocab].astype(np.float64) / temps[:, None].astype(np.float64) + g[:, :vocab]
+    top2 = -np.sort(-keys, axis=1)[:, :2]
+    clear = (top2[:, 0] - top2[:, 1]) >= 1e-5 * np.maximum(1.0, np.abs(top2[:, 0]))
+    assert clear.sum() >= rows // 2
+    assert np.array_equal(got[clear], exact[clear])
 
 
 # ----------------------------------------------------------------------------

@@ -4,6 +4,7 @@ properties the configurations promise (no GPU)."""
 from __future__ import annotations
 
 import numpy as np
+import torch
 import pytest
 
 import workloads as W
@@ -120,3 +121,50 @@ def test_oracle_on_tiny_config_is_finite():
     for blk in range(w.num_blocks):
         if blk not in used:
             assert (kc[blk] == 0x7FC0).all()
+
+
+def _shaped(lens, hq=16, **kw):
+    rng = np.random.default_rng(3)
+    nb = [-(-L // 256) for L in lens]
+    pool = W._Pool(rng, sum(nb))
+    tables = [pool.take(n) for n in nb]
+    setup = [W.Batch([W.Seq(L - 1, 0, t) for L, t in zip(lens, tables)], stream=5)]
+    step = W.Batch([W.Seq(L, L - 1, t) for L, t in zip(lens, tables)], stream=6)
+    w = W.Workload("shaped", 7, hq, 8, 128, 256, sum(nb), max(nb), setup, step, [W.Pass("decode", step)])
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_value_shaping_defaults_leave_draws_unchanged():
+    w = _shaped([300, 40])
+    k, v = W.batch_kv(w, w.setup[0])
+    assert torch.equal(k.view(torch.int16), W.randn_bf16(w.seed, 5, W.TAG_K, k.shape).view(torch.int16))
+    q = W.pass_q(w, w.passes[0])
+    assert torch.equal(q.view(torch.int16), W.randn_bf16(w.seed, 6 + 500_000, W.TAG_Q, q.shape).view(torch.int16))
+
+
+def test_ramp_moves_the_running_max_on_every_key_tile():
+    """The rising-score workload used by the GPU edge cases does what it is for: for every query head, the
+    largest score (log2 units, scale 1/sqrt(128)) of each 32-key tile beats every earlier tile's by more than
+    8, so a lazily rescaled running max has to move on every tile."""
+    w = _shaped([2000], q_bias=1.0, k_ramp=0.03)
+    k, _ = W.batch_kv(w, w.setup[0])
+    q = W.pass_q(w, w.passes[0])
+    s = np.einsum("hd,lhd->hl", q[0].double().numpy().reshape(8, 2, 128)[:, 0], k.double().numpy())
+    s *= w.scale / np.log(2.0)
+    tiles = s[:, : 1984].reshape(8, -1, 32).max(axis=2)
+    rise = tiles[:, 1:] - np.maximum.accumulate(tiles, axis=1)[:, :-1]
+    assert rise.min() > 8.0, rise.min()
+
+
+def test_peaky_queries_widen_the_scores():
+    """q x 8: the scores' spread is about 8 times that of the plain draws (a softmax dominated by few keys)."""
+    w1, w8 = _shaped([1500]), _shaped([1500], q_mult=8.0)
+    k, _ = W.batch_kv(w1, w1.setup[0])
+    spread = []
+    for w in (w1, w8):
+        q = W.pass_q(w, w.passes[0])
+        s = np.einsum("hd,lhd->hl", q[0].double().numpy()[::2], k.double().numpy()) * w.scale
+        spread.append(s.std())
+    assert 7.5 < spread[1] / spread[0] < 8.5

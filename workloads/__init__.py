@@ -80,6 +80,11 @@ class Workload:
     passes: list                     # Passes run after the store
     pad_positions: list = field(default_factory=list)  # store rows that are -1 rows interleaved
     shared_blocks: dict = field(default_factory=dict)  # physical block -> refcount (read-only)
+    # value shaping for softmax edge cases (defaults leave the N(0, 1) draws as they are):
+    # q = q_mult * z + q_bias and K at position p = z + k_ramp * p, in fp32 before the bf16 rounding
+    q_mult: float = 1.0
+    q_bias: float = 0.0
+    k_ramp: float = 0.0
 
     @property
     def scale(self) -> float:
@@ -100,32 +105,56 @@ def _torch():
     return torch
 
 
-def randn_bf16(seed: int, stream: int, tag: int, shape, device="cpu"):
-    """bf16 values rounded (RNE) from fp32 N(0, 1), from a generator seeded by
-    (seed, stream, tag). The same call on the same device returns the same
-    tensor; CPU and GPU generators produce different streams."""
+def randn_f32(seed: int, stream: int, tag: int, shape, device="cpu"):
+    """fp32 N(0, 1) draws from a generator seeded by (seed, stream, tag). The
+    same call on the same device returns the same tensor; CPU and GPU
+    generators produce different streams."""
     torch = _torch()
     g = torch.Generator(device=device)
     g.manual_seed((int(seed) << 40) ^ (int(stream) << 4) ^ int(tag))
-    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
-    return x.to(torch.bfloat16)
+    return torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+
+
+def randn_bf16(seed: int, stream: int, tag: int, shape, device="cpu"):
+    """``randn_f32`` rounded to bf16 (nearest even)."""
+    return randn_f32(seed, stream, tag, shape, device).to(_torch().bfloat16)
 
 
 TAG_K, TAG_V, TAG_Q = 1, 2, 3
 
 
+def row_positions(batch: Batch, extra_rows: int = 0) -> np.ndarray:
+    """Context position of every row of a batch's K/V block (the sequences'
+    tokens num_cached .. seq_len - 1 in order, then 0 for padding rows)."""
+    parts = [np.arange(s.num_cached, s.seq_len) for s in batch.seqs]
+    parts.append(np.zeros(batch.num_pad + extra_rows, dtype=np.int64))
+    return np.concatenate(parts).astype(np.float32)
+
+
 def batch_kv(w: Workload, batch: Batch, device="cpu", extra_rows: int = 0):
-    """K and V rows for a batch: [rows, H_kv, D] bf16 each."""
+    """K and V rows for a batch: [rows, H_kv, D] bf16 each (K shaped by
+    ``w.k_ramp`` when set)."""
+    torch = _torch()
     rows = batch.num_rows + extra_rows
     shape = (rows, w.num_kv_heads, w.head_dim)
-    return (randn_bf16(w.seed, batch.stream, TAG_K, shape, device),
-            randn_bf16(w.seed, batch.stream, TAG_V, shape, device))
+    v = randn_bf16(w.seed, batch.stream, TAG_V, shape, device)
+    if not w.k_ramp:
+        return randn_bf16(w.seed, batch.stream, TAG_K, shape, device), v
+    if w.pad_positions:
+        raise ValueError("k_ramp needs padding rows at the end of the batch")
+    k = randn_f32(w.seed, batch.stream, TAG_K, shape, device)
+    pos = torch.from_numpy(row_positions(batch, extra_rows)).to(device)
+    return (k + w.k_ramp * pos[:, None, None]).to(torch.bfloat16), v
 
 
 def pass_q(w: Workload, p: Pass, device="cpu"):
-    """Query rows for an attention pass: [rows, H_q, D] bf16."""
+    """Query rows for an attention pass: [rows, H_q, D] bf16 (scaled and
+    shifted by ``w.q_mult`` / ``w.q_bias`` when set)."""
     shape = (p.batch.num_rows, w.num_q_heads, w.head_dim)
-    return randn_bf16(w.seed, p.batch.stream + 500_000, TAG_Q, shape, device)
+    if w.q_mult == 1.0 and w.q_bias == 0.0:
+        return randn_bf16(w.seed, p.batch.stream + 500_000, TAG_Q, shape, device)
+    q = randn_f32(w.seed, p.batch.stream + 500_000, TAG_Q, shape, device)
+    return (q * w.q_mult + w.q_bias).to(_torch().bfloat16)
 
 
 def store_kv(w: Workload, device="cpu"):
