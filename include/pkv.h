@@ -30,8 +30,9 @@
  *     are skipped / read as masked), but results for such inputs are
  *     unspecified.
  *   - A call with zero work returns PKV_OK without launching.
- *   - Global state: the thread-local error message and a mutex-guarded,
- *     per-device cache of the decode kernel's resident work-group count.
+ *   - Global state: the thread-local error message, a mutex-guarded,
+ *     per-device cache of the decode kernel's resident work-group count, and
+ *     the scratch array of paged_attn_decode_noalloc (one per GPU).
  *     Calls from different threads on different streams are independent; a
  *     scheduler handle (pkv_sched) belongs to one thread at a time.
  */
@@ -59,7 +60,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 7
+#define PKV_ABI_VERSION 8
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -179,6 +180,34 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int64_t num_blocks, float scale, int32_t max_context_len,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_decode_noalloc — paged_attn_decode without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The same kernels and the same work split as paged_attn_decode, so the
+ * results are bit-identical to that call's. The partial results live in a
+ * fixed 40 MiB device array inside the library (one copy per GPU, allocated
+ * when the library's code object is loaded and held until the process
+ * ends); the call allocates and frees nothing. The array's device address is
+ * looked up once per device, on the first call with that device current.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (on different streams, or from several threads) race and give wrong
+ * results; calls on one stream are ordered and safe. Nothing in the array
+ * needs to start at zero.
+ *
+ * Arguments: as for paged_attn_decode, without workspace / workspace_bytes.
+ * Errors: as for paged_attn_decode, plus PKV_ERR_UNSUPPORTED when the
+ * launch needs more than the 40 MiB (num_q_heads x 1040 bytes x 2 slots
+ * per resident wavefront, plus 4 bytes per sequence: 32 query heads fit on
+ * 1024 resident wavefronts, 64 do not) and PKV_ERR_HIP when the array's
+ * device address cannot be found.
+ */
+pkv_status paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t block_table_stride,
+                                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int64_t num_blocks, float scale, int32_t max_context_len, void* stream);
 
 /*
  * paged_attn_decode_store — kv_store of the step's new token followed by

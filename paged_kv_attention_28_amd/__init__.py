@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     last_error,
     load_library,
     paged_attn_decode,
+    paged_attn_decode_noalloc,
     paged_attn_decode_workspace_size,
     paged_attn_prefill_varlen,
     pkv_prefill_plan,

@@ -20,13 +20,14 @@ PKV_OK = 0
 STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "HIP", 4: "WORKSPACE"}
 
 EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
-           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_store",
+           "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_noalloc",
+           "paged_attn_decode_store",
            "paged_attn_prefill_varlen",
            "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
            "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks", "pkv_decode_graphs_create",
            "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy", "rope_kv_store", "pkv_rope_cos_sin",
            "sample_temperature_workspace_size", "sample_temperature")
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class PkvError(RuntimeError):
@@ -87,6 +88,9 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_decode.restype = c_i32
     lib.paged_attn_decode.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, c_i32,
                                       c_i64, c_f32, c_i32, c_vp, c_size, c_vp]
+    lib.paged_attn_decode_noalloc.restype = c_i32
+    lib.paged_attn_decode_noalloc.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp, c_i32, c_i32, c_i32, c_i32,
+                                              c_i32, c_i64, c_f32, c_i32, c_vp]
     lib.paged_attn_decode_store.restype = c_i32
     lib.paged_attn_decode_store.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp,
                                             c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_f32, c_i32, c_vp, c_size,
@@ -445,6 +449,26 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
                                _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, N,
                                float(scale), int(max_context_len), ws_ptr, ws_bytes, _stream(stream))
     _check("paged_attn_decode", st)
+
+
+def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                              stream=None):
+    """paged_attn_decode on the library's own scratch array (no workspace argument); same arguments otherwise."""
+    torch = _torch()
+    lib = load_library()
+    S, Hq, D = q.shape
+    N, B, Hkv, _ = k_cache.shape
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] < S or context_lens.shape[0] < S:
+        raise ValueError("block_tables / context_lens do not cover the batch")
+    st = lib.paged_attn_decode_noalloc(_dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+                                       _dev(k_cache, "k_cache", torch.bfloat16),
+                                       _dev(v_cache, "v_cache", torch.bfloat16),
+                                       _dev(block_tables, "block_tables", torch.int32), block_tables.stride(0),
+                                       _dev(context_lens, "context_lens", torch.int32), S, Hq, Hkv, D, B, N,
+                                       float(scale), int(max_context_len), _stream(stream))
+    _check("paged_attn_decode_noalloc", st)
 
 
 def paged_attn_decode_store(out, q, key, value, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale,

@@ -718,12 +718,41 @@ struct Layout {
   size_t header_bytes, ml_bytes, o_bytes;  // header = steps per wavefront + step prefix
 };
 
-Layout workspace_layout(int num_seqs, int num_q_heads) {
+// Workspace for `waves` wavefronts (2 partial slots each). The caller-owned
+// workspace is sized for the grid cap, so its size does not depend on the
+// device; the library's own scratch (paged_attn_decode_noalloc) for the
+// launch's actual wavefront count.
+Layout workspace_layout(int num_seqs, int num_q_heads, int waves = kWavesCap) {
   Layout lo;
   lo.header_bytes = ((size_t)(num_seqs + 2) * 4 + 255) & ~(size_t)255;
-  lo.ml_bytes = ((size_t)kWavesCap * 2 * num_q_heads * 2 * 4 + 255) & ~(size_t)255;
-  lo.o_bytes = (size_t)kWavesCap * 2 * num_q_heads * kHeadDim * 4;
+  lo.ml_bytes = ((size_t)waves * 2 * num_q_heads * 2 * 4 + 255) & ~(size_t)255;
+  lo.o_bytes = (size_t)waves * 2 * num_q_heads * kHeadDim * 4;
   return lo;
+}
+
+// The decode workspace of paged_attn_decode_noalloc: a fixed device array,
+// one copy per GPU (allocated when the code object is loaded, held until
+// the process ends). 40 MiB covers 32 query heads on 1024 resident
+// wavefronts (one work-group of four per CU on 256 CUs).
+constexpr size_t kScratchBytes = (size_t)40 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+// This device's address of `scratch`, looked up once per device with that
+// device current (each GPU holds its own copy at its own address); nullptr
+// on error. Host code uses only this address, never the array's name.
+char* scratch_address() {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return static_cast<char*>(addr[dev]);
 }
 
 template <int G, int HKV>
@@ -800,11 +829,13 @@ extern "C" size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num
 namespace pkv {
 namespace {
 
+// use_scratch: the workspace is the library's `scratch` array
+// (paged_attn_decode_noalloc; workspace and workspace_bytes are ignored).
 pkv_status decode_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
                        int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int64_t num_blocks, float scale, int32_t max_context_len, void* workspace,
-                       size_t workspace_bytes, void* stream, const NewRows& nr) {
+                       size_t workspace_bytes, void* stream, const NewRows& nr, bool use_scratch = false) {
   if (num_seqs < 0 || num_blocks < 0 || max_context_len < 0 || block_table_stride < 0)
     return fail(PKV_ERR_INVALID, "paged_attn_decode: negative size");
   if (head_dim != kHeadDim) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: head_dim %d (128 only)", head_dim);
@@ -832,17 +863,16 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   // the kernels count two-token steps (a step holds at least two tokens) in 32-bit integers
   if ((int64_t)num_seqs * ((max_context_len + 1) / 2) > INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: num_seqs x max_context_len / 2 exceeds 2^31 - 1 steps");
-  const size_t ws = paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len);
-  if (!workspace || workspace_bytes < ws)
-    return fail(PKV_ERR_WORKSPACE, "paged_attn_decode: workspace of %zu bytes needed, got %zu", ws, workspace_bytes);
-  if (reinterpret_cast<uintptr_t>(workspace) & 255)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: workspace must be 256-byte aligned");
+  if (!use_scratch) {
+    const size_t ws =
+        paged_attn_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len);
+    if (!workspace || workspace_bytes < ws)
+      return fail(PKV_ERR_WORKSPACE, "paged_attn_decode: workspace of %zu bytes needed, got %zu", ws,
+                  workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255)
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: workspace must be 256-byte aligned");
+  }
 
-  const Layout lo = workspace_layout(num_seqs, num_q_heads);
-  char* wsb = static_cast<char*>(workspace);
-  int32_t* header = reinterpret_cast<int32_t*>(wsb);
-  float* part_ml = reinterpret_cast<float*>(wsb + lo.header_bytes);
-  float* part_o = reinterpret_cast<float*>(wsb + lo.header_bytes + lo.ml_bytes);
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = stream_lds(num_seqs);
   // Part of the CUs, by the query heads per KV head: measured on MI355X (256 CUs) with 192, 224 and 256
@@ -852,6 +882,26 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   const int resident = resident_wgs(pick_kernel(G, num_kv_heads), lds);
   if (resident <= 0) return fail(PKV_ERR_HIP, "paged_attn_decode: cannot query the device");
   const int grid = resident < 8 || G >= 4 ? resident : resident * 3 / 4;
+
+  Layout lo;
+  char* wsb;
+  if (use_scratch) {
+    lo = workspace_layout(num_seqs, num_q_heads, grid * 4);
+    const size_t need = lo.header_bytes + lo.ml_bytes + lo.o_bytes;
+    if (need > kScratchBytes)
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "paged_attn_decode_noalloc: %d query heads on %d wavefronts need %zu bytes of workspace, more "
+                  "than the library's %zu-byte scratch (use paged_attn_decode with a caller workspace)",
+                  num_q_heads, grid * 4, need, kScratchBytes);
+    wsb = scratch_address();
+    if (!wsb) return fail(PKV_ERR_HIP, "paged_attn_decode_noalloc: cannot find the device's scratch array");
+  } else {
+    lo = workspace_layout(num_seqs, num_q_heads);
+    wsb = static_cast<char*>(workspace);
+  }
+  int32_t* header = reinterpret_cast<int32_t*>(wsb);
+  float* part_ml = reinterpret_cast<float*>(wsb + lo.header_bytes);
+  float* part_o = reinterpret_cast<float*>(wsb + lo.header_bytes + lo.ml_bytes);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -916,6 +966,18 @@ extern "C" pkv_status paged_attn_decode(void* out, const void* q, const void* k_
   return pkv::decode_call(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs,
                           num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, max_context_len,
                           workspace, workspace_bytes, stream, none);
+}
+
+extern "C" pkv_status paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                                const int32_t* block_tables, int32_t block_table_stride,
+                                                const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                int64_t num_blocks, float scale, int32_t max_context_len,
+                                                void* stream) {
+  const pkv::NewRows none{nullptr, nullptr, 0, 0, nullptr, 0, nullptr, nullptr};
+  return pkv::decode_call(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs,
+                          num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, max_context_len,
+                          nullptr, 0, stream, none, true);
 }
 
 extern "C" pkv_status paged_attn_decode_store(void* out, const void* q, const void* key, int64_t key_token_stride,
