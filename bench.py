@@ -24,8 +24,12 @@ per call) against the HBM peak. ``hbm_copy_ceiling`` is torch's own copy over
 2 GiB. ``trace_replay`` replays
 the 28-layer scheduler trace (256 requests) and reports decode GB/s, prefill
 TFLOP/s and kernel-only tokens/s from events around each layer's kernels. ``cpu_baseline`` times the
-fp64 oracle on the same decode step on the host (about 10 s of repeats)
-before the GPU is initialised.
+fp64 oracle on the host's cores (one single-threaded worker per core, one
+sequence per task) over configurations 1-4 in full and a labelled sample of
+the trace replay, before the GPU is initialised; its ``value`` is the decode
+workload's step. The decode step's host preparation works on the batch's
+sequence state held as arrays (``binding.StepPrep``), as a scheduler keeps
+it: one C call per step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-prefill] [--no-graph] [--no-back-to-back] [--no-trace] [--no-fused]
@@ -109,56 +113,194 @@ def prefill_work(w: W.Workload) -> dict:
 
 
 # ----------------------------------------------------------------------------
-# CPU baseline: the oracle, on the host, before any GPU work
+# CPU baseline: the oracle on the host's cores, before any GPU work
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(w: W.Workload) -> dict:
+CPU_WORKERS_CAP = 16   # the host cores one GPU's share of the box holds
+_BANK_ROWS = 8192      # random bf16 token rows each worker reuses as K/V/q values
+_worker = {}
+
+
+def _cpu_worker_init():
+    """Pool worker: BLAS on one thread; a bank of random bf16 bit patterns
+    (the oracle's time does not depend on the values, so the bank is reused
+    for every sequence's K, V and q)."""
     try:
         from threadpoolctl import threadpool_limits
+        _worker["limit"] = threadpool_limits(limits=1)
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    from tests import oracle_side as O
+        pass
+    rng = np.random.default_rng(os.getpid())
+    x = rng.standard_normal((_BANK_ROWS, 1024)).astype(np.float32)
+    u = x.view(np.uint32)
+    _worker["bank"] = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)   # bf16, nearest even
+
+
+def _bank_rows(n: int, width: int, start: int) -> np.ndarray:
+    """n rows of `width` bf16 bit patterns from the bank (wrapping)."""
+    bank = _worker["bank"]
+    idx = (start + np.arange(n)) % _BANK_ROWS
+    return bank[idx, :width]
+
+
+def _task_seq(src, a: int, b: int):
+    """(sequence state, H_q, H_kv, kind) of task (src, a, b): src 1-4 = config, a = pass index; src 5 = the
+    scheduler-trace replay, a = step index."""
+    key = ("w", src)
+    if key not in _worker:
+        if src == 5:
+            from oracle import sched as OS
+            from workloads import sched as S
+            prompts, outputs = S.requests()
+            steps, _, _ = OS.replay(prompts, outputs, S.POOL_BLOCKS, S.MAX_NUM_SEQS, S.MAX_BATCHED_TOKENS)
+            _worker[key] = steps
+        else:
+            _worker[key] = W.make(src)
+    if src == 5:
+        st = _worker[key][a]
+        return st.batch.seqs[b], 16, 8, st.kind
+    w = _worker[key]
+    p = w.passes[a]
+    return p.batch.seqs[b], w.num_q_heads, w.num_kv_heads, p.kind
+
+
+def _oracle_task(spec):
+    """One unit of the CPU baseline: one sequence of one pass. Its inputs (a compact pool holding the
+    sequence's blocks with its cached context, its new K/V rows and queries) are built first, untimed; then
+    the oracle's own step is timed: metadata (prepare_step_ref), the store of the new rows (kv_store_ref) and
+    the attention (decode_ref or prefill_ref). Returns (seconds, worker pid)."""
     from oracle import paged as op
-
-    log("[bench] cpu baseline: building the oracle's caches on the host ...")
-    t = time.perf_counter()
-    # setup (history) stores are not part of a step
-    w_setup_only = W.Workload(w.name, w.seed, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
-                              w.num_blocks, w.max_blocks_per_seq, w.setup, W.Batch([], stream=999), [])
-    kc, vc = O.build_caches(w_setup_only, device="cpu")
-    k, v = W.store_kv(w, "cpu")
-    kb, vb = O.bits(k), O.bits(v)
-    p = w.passes[0]
-    q = O.bits(W.pass_q(w, p, "cpu"))
-    log(f"[bench] cpu baseline: inputs ready in {time.perf_counter() - t:.1f}s; timing the oracle step")
-
-    def run():
-        slots, cu, ctx, bt = O.metadata(w, p.batch)
-        kc2, vc2 = op.kv_store_ref(kc, vc, kb, vb, slots)
-        return op.decode_ref(q, kc2, vc2, bt, ctx, w.scale)
-
-    def timed():  # repeat the step until about 10 s of CPU work (at least 3 runs); mean per step
-        runs, t0 = 0, time.perf_counter()
-        while runs < 3 or (time.perf_counter() - t0 < 10.0 and runs < 40):
-            run()
-            runs += 1
-        return (time.perf_counter() - t0) / runs, runs
-
-    cores = 1
-    if threadpool_limits is not None:
-        with threadpool_limits(limits=1):
-            dt, runs = timed()
+    src, a, b = spec
+    seq, hq, hkv, kind = _task_seq(src, a, b)
+    L, c = seq.seq_len, seq.num_cached
+    nb = -(-L // W.BLOCK_SIZE)
+    table = list(range(nb))                # outputs do not depend on physical block ids (a pinned property)
+    width = hkv * W.HEAD_DIM
+    kc = np.full((nb, W.BLOCK_SIZE, hkv, W.HEAD_DIM), 0x7FC0, dtype=np.uint16)
+    vc = kc.copy()
+    kc.reshape(-1, width)[:c] = _bank_rows(c, width, 0)
+    vc.reshape(-1, width)[:c] = _bank_rows(c, width, 7)
+    n = L - c
+    key = _bank_rows(n, width, c).reshape(n, hkv, W.HEAD_DIM)
+    value = _bank_rows(n, width, c + 11).reshape(n, hkv, W.HEAD_DIM)
+    q = np.concatenate([_bank_rows(n, 1024, 3 + 97 * i) for i in range(-(-hq * W.HEAD_DIM // 1024))], axis=1)
+    q = np.ascontiguousarray(q[:, :hq * W.HEAD_DIM]).reshape(n, hq, W.HEAD_DIM)
+    scale = 1.0 / float(np.sqrt(W.HEAD_DIM))
+    t0 = time.perf_counter()
+    slots, cu, ctx, bt = op.prepare_step_ref([L], [c], [table], W.BLOCK_SIZE, nb)
+    kc2, vc2 = op.kv_store_ref(kc, vc, key, value, slots)
+    if kind == "decode":
+        op.decode_ref(q, kc2, vc2, bt, ctx, scale)
     else:
-        dt, runs = timed()
-        cores = os.cpu_count() or 1
-    b = decode_bytes(w)
-    gbs = (b["attn"] + b["store"]) / dt / 1e9
-    log(f"[bench] cpu baseline: oracle step {dt:.2f}s (mean of {runs}) -> {gbs:.4f} GB/s")
-    return {"value": round(gbs, 5), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "seconds": round(dt, 3), "runs": runs,
-            "sample": f"one full decode step of the decode workload (store of 272 rows + decode of 256 "
-                      f"sequences and 16 padding rows), repeated {runs} times (about 10 s), fp64 numpy oracle, "
-                      f"BLAS limited to 1 thread; host-generated values of the same shapes"}
+        op.prefill_ref(q, cu, ctx, kc2, vc2, bt, scale)
+    return time.perf_counter() - t0, os.getpid()
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _pool_run(pool, tasks):
+    """Runs tasks over the pool; returns (summed oracle seconds, the busiest worker's oracle seconds, wall
+    seconds including the untimed input building)."""
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_task, tasks, chunksize=1)
+    wall = time.perf_counter() - t0
+    per = {}
+    for dt, pid in res:
+        per[pid] = per.get(pid, 0.0) + dt
+    return sum(dt for dt, _ in res), max(per.values()), wall
+
+
+def cpu_baseline() -> dict:
+    """The fp64 oracle on the host: one single-threaded worker per core (capped at one GPU's share of the
+    box), one sequence per task, over every configuration: 1-4 in full and a labelled sample of 5 with its
+    extrapolation. `parallel_s` is the busiest worker's summed oracle time (the oracle's wall time on these
+    cores with free input building); rates use it."""
+    import multiprocessing as mp
+    from oracle import sched as OS
+    from workloads import sched as S
+    cores = min(len(os.sched_getaffinity(0)), CPU_WORKERS_CAP)
+    log(f"[bench] cpu baseline: oracle on {cores} worker processes ({len(os.sched_getaffinity(0))} cores visible, "
+        f"{_cpu_model()})")
+    entries = {}
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_cpu_worker_init) as pool:
+        for k in (1, 2, 3, 4):
+            w = W.make(k)
+            tasks = [(k, a, b) for a, p in enumerate(w.passes) for b in range(len(p.batch.seqs))]
+            cpu_s, par_s, wall = _pool_run(pool, tasks)
+            e = {"sequences": len(tasks), "cpu_s": round(cpu_s, 3), "parallel_s": round(par_s, 3),
+                 "wall_s_with_input_building": round(wall, 2)}
+            if k in (2, 4):
+                db = decode_bytes(w)
+                e["gbs"] = round((db["attn"] + db["store"]) / par_s / 1e9, 5)
+                e["what"] = "decode step: store of the new token + decode, every sequence"
+            elif k == 3:
+                pw = prefill_work(w)
+                e["tflops"] = round(pw["flops"] / par_s / 1e12, 6)
+                e["what"] = "prefill step: store of the new tokens + varlen causal prefill, every sequence"
+            else:
+                e["what"] = "tiny: the decode pass and the prefill pass, every sequence"
+            entries[f"config{k}"] = e
+            log(f"[bench] cpu baseline config {k}: {len(tasks)} sequences, {cpu_s:.2f} cpu-s, {par_s:.2f} s on "
+                f"{cores} workers ({wall:.1f} s with input building)")
+        # config 5: the first prefill, the first re-prefill after a preemption and four decode steps (one layer
+        # each), then an extrapolation to every step and all 28 layers by work (context tokens for decode,
+        # unmasked pairs for prefill)
+        prompts, outputs = S.requests()
+        steps, _, _ = OS.replay(prompts, outputs, S.POOL_BLOCKS, S.MAX_NUM_SEQS, S.MAX_BATCHED_TOKENS)
+        pre = next(i for i, st in enumerate(steps) if st.preempted)
+        re_pre = next(i for i in range(pre, len(steps)) if steps[i].kind == "prefill")
+        dec = [i for i, st in enumerate(steps) if st.kind == "decode"]
+        sample = sorted({0, re_pre, dec[0], dec[len(dec) // 3], dec[2 * len(dec) // 3], dec[-1]})
+
+        def work(st):
+            if st.kind == "decode":
+                return sum(s.seq_len for s in st.batch.seqs)
+            return sum((s.seq_len - s.num_cached) * s.num_cached + (s.seq_len - s.num_cached) *
+                       (s.seq_len - s.num_cached + 1) // 2 for s in st.batch.seqs)
+
+        rate = {"decode": [0.0, 0], "prefill": [0.0, 0]}
+        cpu5 = par5 = 0.0
+        for i in sample:
+            st = steps[i]
+            cpu_s, par_s, _ = _pool_run(pool, [(5, i, b) for b in range(len(st.batch.seqs))])
+            cpu5 += cpu_s
+            par5 += par_s
+            rate[st.kind][0] += cpu_s
+            rate[st.kind][1] += work(st)
+        est_cpu = 0.0
+        for st in steps:
+            r = rate[st.kind]
+            est_cpu += work(st) * r[0] / r[1]
+        est_cpu *= S.NUM_LAYERS
+        entries["config5"] = {"sampled_steps": sample, "sampled_step_layers": len(sample), "cpu_s": round(cpu5, 3),
+                              "parallel_s": round(par5, 3),
+                              "us_per_step_layer_parallel": round(par5 / len(sample) * 1e6, 1),
+                              "extrapolated_cpu_s_all_steps_28_layers": round(est_cpu, 1),
+                              "extrapolated_parallel_s": round(est_cpu / cores, 1),
+                              "what": f"extrapolation (labelled): {len(steps)} steps x {S.NUM_LAYERS} layers from "
+                                      f"{len(sample)} sampled step-layers, scaled by decode context tokens and "
+                                      f"prefill pairs"}
+        log(f"[bench] cpu baseline config 5: {len(sample)} sampled step-layers in {par5:.2f} s on {cores} workers; "
+            f"all {len(steps)} steps x {S.NUM_LAYERS} layers extrapolated to {est_cpu / cores:.0f} s")
+    head = entries["config2"]
+    return {"value": head["gbs"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "cores_visible": len(os.sched_getaffinity(0)),
+            "sample": "configs 1-4 in full (config 4: all 512 sequences), config 5 sampled (6 step-layers, "
+                      "extrapolation labelled); value = config 2's decode step (store + decode of 256 sequences); "
+                      "fp64 numpy oracle, one single-threaded worker per core, one sequence per task, each "
+                      "sequence on a compact pool of its own blocks; input values are random bf16 bit patterns "
+                      "of the workloads' shapes (the oracle's time does not depend on them), built outside the "
+                      "timed region",
+            "configs": entries}
 
 
 # ----------------------------------------------------------------------------
@@ -208,6 +350,28 @@ def fused_steps(runner, steps: int, warmup: int, torch):
     wall = time.perf_counter() - t0
     call_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     return wall / steps * 1e3, float(call_ms.mean())
+
+
+def cold_warm(torch, runner, reps: int = 50) -> dict:
+    """The decode attention call alone, `reps` times each way, HIP events on its stream: warm (calls back to
+    back, the previous call's K/V partly still in L2 and the Infinity Cache) and cold (1 GiB of unrelated data
+    written just before each call, outside the events, so the caches hold none of its K/V and are full of
+    dirty lines, as after a large GEMM). Medians in microseconds."""
+    flush = torch.empty(2**30 // 4, dtype=torch.int32, device=runner.q.device)
+    out = {}
+    for mode in ("warm", "cold"):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        runner.attention_only()
+        for i, e in enumerate(ev):
+            if mode == "cold":
+                flush.fill_(i)
+            e[0].record()
+            runner.attention_only()
+            e[1].record()
+        torch.cuda.synchronize()
+        out[mode] = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+    del flush
+    return out
 
 
 def rope_store_rate(torch, w, runner, reps: int):
@@ -512,7 +676,7 @@ def main():
     wd = W.make(2)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wd)
+        cpu = cpu_baseline()
 
     import torch
     from paged_kv_attention_28_amd import harness as H
@@ -536,6 +700,10 @@ def main():
     achieved = db["attn"] / (attn_avg * 1e-3) / 1e9
     log(f"[bench] decode step {ms * 1e3:.1f} us wall; store {store_ms.mean() * 1e3:.1f} us, "
         f"attention {attn_avg * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
+    cw = cold_warm(torch, runner)
+    log(f"[bench] decode attention, median of 50: warm {cw['warm']:.1f} us "
+        f"({db['attn'] / (cw['warm'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%}), cold (1 GiB written before each call) "
+        f"{cw['cold']:.1f} us ({db['attn'] / (cw['cold'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%})")
     fused = None
     if not args.no_fused:
         fms, fcall = fused_steps(runner, args.steps, args.warmup, torch)
@@ -617,7 +785,14 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "paged_attn_decode call (decode_stream_kernel + decode_merge_kernel), HIP events "
                                "on its stream, mean over the timed steps",
-                     "algorithmic_bytes": db["attn"], "us": round(attn_avg * 1e3, 2)},
+                     "algorithmic_bytes": db["attn"], "us": round(attn_avg * 1e3, 2),
+                     "warm_median_us": round(cw["warm"], 2),
+                     "warm_median_frac": round(db["attn"] / (cw["warm"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "cold_median_us": round(cw["cold"], 2),
+                     "cold_median_frac": round(db["attn"] / (cw["cold"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "cold_note": "median of 50 calls, each after 1 GiB of unrelated data was written (outside the "
+                                  "events): nothing of the call's K/V in L2 or the Infinity Cache; warm: 50 calls "
+                                  "back to back"},
         "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
         "decode_step_fused": fused,
         "prefill": prefill,

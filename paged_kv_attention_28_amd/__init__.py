@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     SchedStep,
     Scheduler,
     StepMeta,
+    StepPrep,
     kv_store,
     last_error,
     load_library,

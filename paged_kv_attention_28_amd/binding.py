@@ -202,6 +202,62 @@ def pkv_prepare_step(seq_lens, num_cached, block_tables, block_size: int, max_bl
                     n, mq.value, mc.value)
 
 
+class StepPrep:
+    """``pkv_prepare_step`` (and, for a prefill step, ``pkv_prefill_plan``)
+    on a sequence state held as arrays, the form a scheduler keeps it in
+    (``pkv_sched_batch`` hands out the same CSR arrays): the arrays and the
+    calls' pointer arguments are built once, so each call costs one C call
+    per function writing into ``out`` (e.g. pinned buffers). Calling it
+    again recomputes the metadata from the (possibly updated) arrays
+    ``seq_lens``, ``num_cached`` and ``bt_data``."""
+
+    def __init__(self, seq_lens, num_cached, block_tables, block_size: int, max_blocks_per_seq: int,
+                 num_pad: int, out, plan_heads=None, plan_out=None):
+        self.lib = load_library()
+        S = len(seq_lens)
+        self.seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        self.num_cached = np.ascontiguousarray(num_cached, dtype=np.int32)
+        self.bt_offsets = np.zeros(S + 1, dtype=np.int64)
+        if S:
+            self.bt_offsets[1:] = np.cumsum([len(t) for t in block_tables])
+        self.bt_data = (np.ascontiguousarray(np.concatenate([np.asarray(t, dtype=np.int32) for t in block_tables]))
+                        if S and self.bt_offsets[-1] else np.zeros(1, dtype=np.int32))
+        self.rows = S + num_pad
+        self.mb = max_blocks_per_seq
+        self.out = out
+        slots, cu, ctx, bt = out
+        for a in out:
+            if a.dtype != np.int32 or not a.flags.c_contiguous:
+                raise ValueError("out arrays must be contiguous int32")
+        self._nt, self._mq, self._mc = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        self._args = (S, _i32p(self.seq_lens), _i32p(self.num_cached), _i32p(self.bt_data),
+                      self.bt_offsets.ctypes.data_as(P_I64), int(num_pad), int(block_size), int(max_blocks_per_seq),
+                      _i32p(slots), int(slots.size), _i32p(cu), _i32p(ctx), _i32p(bt), ctypes.byref(self._nt),
+                      ctypes.byref(self._mq), ctypes.byref(self._mc))
+        self.plan_out = plan_out
+        self._n_items = ctypes.c_int64(0)
+        if plan_heads is not None:
+            if plan_out.dtype != np.int32 or not plan_out.flags.c_contiguous:
+                raise ValueError("plan_out must be a contiguous int32 array")
+            self._plan_args = (self.rows, _i32p(cu), _i32p(ctx), int(plan_heads[0]), int(plan_heads[1]),
+                               _i32p(plan_out), plan_out.size // 2, ctypes.byref(self._n_items))
+        else:
+            self._plan_args = None
+
+    def __call__(self):
+        """Returns (StepMeta, number of plan items or 0)."""
+        _check("pkv_prepare_step", self.lib.pkv_prepare_step(*self._args))
+        slots, cu, ctx, bt = self.out
+        n = self._nt.value
+        m = StepMeta(slots[:n], cu[:self.rows + 1], ctx[:self.rows],
+                     bt[:self.rows * self.mb].reshape(self.rows, self.mb), n, self._mq.value, self._mc.value)
+        items = 0
+        if self._plan_args is not None:
+            _check("pkv_prefill_plan", self.lib.pkv_prefill_plan(*self._plan_args))
+            items = self._n_items.value
+        return m, items
+
+
 def pkv_prefill_plan(cu_seqlens_q, context_lens, num_q_heads: int, num_kv_heads: int, out=None) -> np.ndarray:
     """Call ``pkv_prefill_plan`` on host arrays; returns int32 [n, 2] items.
     ``out`` may be a preallocated host int32 array of 2 * capacity elements

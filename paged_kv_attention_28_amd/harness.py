@@ -146,20 +146,26 @@ class StepRunner:
         self.max_q_len = m0.max_q_len
         self.max_ctx = m0.max_context_len
         self.workspace = (decode_workspace(w, rows, self.max_ctx, dev) if p.kind == "decode" else None)
+        # the batch's sequence state as arrays (as a scheduler holds it), one preparation per pinned buffer set
+        b = p.batch
+        heads = (w.num_q_heads, w.num_kv_heads) if p.kind == "prefill" else None
+        self.preps = []
+        for k in range(2):
+            flat = self.pinned[k].numpy()
+            self.preps.append(B.StepPrep([s.seq_len for s in b.seqs], [s.num_cached for s in b.seqs],
+                                         [s.block_table for s in b.seqs], w.block_size, w.max_blocks_per_seq,
+                                         b.num_pad, tuple(flat[offs[i]:offs[i + 1]] for i in range(4)), heads,
+                                         flat[offs[5]:offs[6]]))
         self.i = 0
 
     def prepare_and_upload(self):
-        w, p = self.dw.w, self.p
+        """Host step preparation (pkv_prepare_step, plus pkv_prefill_plan for a
+        prefill step) into the next pinned buffer set, then one upload."""
         k = self.i & 1
         self.i += 1
         if self.events[k] is not None:
             self.events[k].synchronize()
-        flat = self.pinned[k].numpy()
-        o = self.offs
-        m = meta(w, p.batch, out=tuple(flat[o[i]:o[i + 1]] for i in range(4)))
-        if p.kind == "prefill":
-            self.num_items = B.pkv_prefill_plan(m.cu_seqlens_q, m.context_lens, w.num_q_heads, w.num_kv_heads,
-                                                out=flat[o[5]:o[6]]).shape[0]
+        _, self.num_items = self.preps[k]()
         self.dev_flat.copy_(self.pinned[k], non_blocking=True)
         ev = torch.cuda.Event()
         ev.record()

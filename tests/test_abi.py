@@ -255,3 +255,30 @@ def test_prefill_plan_validation(lib):
     assert lib.pkv_prefill_plan(1, p32(cu), p32(ctx), 16, 8, p32(items), 8, ctypes.byref(n)) == 0
     assert items.reshape(8, 2).tolist() == [[0, g] for g in range(8)]
     assert lib.pkv_prefill_plan(0, None, None, 16, 8, None, 0, ctypes.byref(n)) == 0 and n.value == 0
+
+
+@pytest.mark.parametrize("k", [2, 3])
+def test_step_prep_matches_prepare_step_and_plan(k):
+    """StepPrep (the arrays-once form of the step preparation the bench's step uses) writes the same metadata
+    as pkv_prepare_step, which matches the oracle, and the same prefill plan as pkv_prefill_plan."""
+    w = W.make(k)
+    b = w.passes[0].batch
+    rows = len(b.seqs) + b.num_pad
+    T = b.num_rows
+    out = (np.zeros(T, np.int32), np.zeros(rows + 1, np.int32), np.zeros(rows, np.int32),
+           np.zeros(rows * w.max_blocks_per_seq, np.int32))
+    cap = P.prefill_plan_capacity(T, rows, w.num_q_heads, w.num_kv_heads)
+    plan = np.zeros(2 * cap, np.int32)
+    heads = (w.num_q_heads, w.num_kv_heads) if k == 3 else None
+    prep = P.StepPrep([s.seq_len for s in b.seqs], [s.num_cached for s in b.seqs], [s.block_table for s in b.seqs],
+                      w.block_size, w.max_blocks_per_seq, b.num_pad, out, heads, plan)
+    for _ in range(2):                      # a second call rewrites the same buffers identically
+        m, items = prep()
+        slots, cu, ctx, bt = metadata(w, b)
+        assert np.array_equal(m.slot_mapping, slots) and np.array_equal(m.cu_seqlens_q, cu)
+        assert np.array_equal(m.context_lens, ctx) and np.array_equal(m.block_tables, bt)
+        if k == 3:
+            ref = P.pkv_prefill_plan(cu, ctx, w.num_q_heads, w.num_kv_heads)
+            assert items == ref.shape[0] and np.array_equal(plan[:2 * items].reshape(-1, 2), ref)
+        else:
+            assert items == 0
