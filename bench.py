@@ -2,18 +2,21 @@
 
 A step is one pass of the whole path over one batch, as an engine runs it:
 host step preparation (slot mapping, lengths, padded block tables) into
-pinned buffers, upload, kv_store of the step's K/V, then attention.
-``decode_step_fused`` times the same decode step with the store inside the
-attention call (paged_attn_decode_store).
+pinned buffers, one upload, the store of the step's K/V, then attention.
 
 Headline (``value``): the decode step of the 256-sequence decode workload
 (contexts U[100, 2048], 16 Q / 8 KV heads, head dim 128, bf16, block 256,
-batch padded to 272 rows) in GB/s of algorithmic HBM bytes (K/V context read
-once, q, out, block-table entries and lengths, plus 8 KiB stored per real
-token) per wall-clock step. ``roofline`` reports the decode attention call
-(persistent stream-K kernel + merge kernel) timed with HIP events on its
-stream against the 8 TB/s HBM peak; ``traffic`` is the HBM bytes per call from
-the committed rocprofv3 counter summary, or null once the kernel changed. ``prefill`` reports the chunked-prefill step (16384-token
+batch padded to 272 rows), with the store of the new tokens fused into the
+decode call (paged_attn_decode_store), in GB/s of algorithmic HBM bytes (K/V
+context read once, q, out, block-table entries and lengths, plus 8 KiB
+stored per real token) per wall-clock step. ``roofline`` reports that call
+(persistent stream-K kernel with the fused store + merge kernel) timed with
+HIP events on its stream against the 8 TB/s HBM peak (algorithmic bytes: the
+attention's plus the 4 KiB of new rows written per sequence), with warm and
+cold (caches flushed by a 1 GiB write) medians; ``traffic`` is the HBM bytes
+per call from the committed rocprofv3 counter summary, or null once the
+kernel changed. ``decode_step_two_calls`` times the same step as kv_store
+followed by paged_attn_decode. ``prefill`` reports the chunked-prefill step (16384-token
 budget) in TFLOP/s of unmasked attention flops against the 2.5 PFLOP/s bf16
 MFMA peak, its roofline fraction max(t_MFMA, t_HBM) / t (HBM bytes: q, out and
 the distinct context K/V rows), and the same call launched back to back for
@@ -89,7 +92,9 @@ def decode_bytes(w: W.Workload) -> dict:
     qo = 2 * rows * w.num_q_heads * w.head_dim * 2
     bt = sum(-(-s.seq_len // w.block_size) for s in real) * 4 + rows * 4
     store = sum(s.seq_len - s.num_cached for s in real) * w.num_kv_heads * w.head_dim * 2 * 4
-    return {"attn": kv + qo + bt, "store": store, "kv": kv}
+    # the fused call (paged_attn_decode_store) reads the new token's K/V once (part of the context) and writes it
+    written = sum(s.seq_len - s.num_cached for s in real) * w.num_kv_heads * w.head_dim * 2 * 2
+    return {"attn": kv + qo + bt, "store": store, "kv": kv, "fused_call": kv + qo + bt + written}
 
 
 def prefill_work(w: W.Workload) -> dict:
@@ -317,13 +322,14 @@ def time_steps(runner, steps: int, warmup: int, torch):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        runner.prepare_and_upload()
+        k = runner.prepare_and_upload(record_guard=False)
         e = evs[i]
         e[0].record()
         runner.store_only()
         e[1].record()
         runner.attention_only()
         e[2].record()
+        runner.guard(k, e[2])        # the step's last event also guards its pinned buffer set
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     store_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
@@ -332,9 +338,10 @@ def time_steps(runner, steps: int, warmup: int, torch):
 
 
 def fused_steps(runner, steps: int, warmup: int, torch):
-    """The decode step with the store fused into the attention call
-    (paged_attn_decode_store): wall-clock per step over `steps` steps and the
-    mean HIP-event time of the call on its stream."""
+    """The decode step as the engine runs it: host preparation, one upload and
+    paged_attn_decode_store (the step's store fused into the attention call).
+    Wall-clock per step over `steps` steps, bracketed by synchronize, and the
+    HIP-event time of every call on its stream (ms)."""
     for _ in range(warmup):
         runner.prepare_and_upload()
         runner.fused_only()
@@ -342,34 +349,37 @@ def fused_steps(runner, steps: int, warmup: int, torch):
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        runner.prepare_and_upload()
+        k = runner.prepare_and_upload(record_guard=False)
         evs[i][0].record()
         runner.fused_only()
         evs[i][1].record()
+        runner.guard(k, evs[i][1])   # the call's end event also guards the step's pinned buffer set
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     call_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    return wall / steps * 1e3, float(call_ms.mean())
+    return wall / steps * 1e3, call_ms
 
 
-def cold_warm(torch, runner, reps: int = 50) -> dict:
-    """The decode attention call alone, `reps` times each way, HIP events on its stream: warm (calls back to
-    back, the previous call's K/V partly still in L2 and the Infinity Cache) and cold (1 GiB of unrelated data
-    written just before each call, outside the events, so the caches hold none of its K/V and are full of
-    dirty lines, as after a large GEMM). Medians in microseconds."""
+def cold_warm(torch, runner, call_bytes: int, reps: int = 50) -> dict:
+    """The decode step's call (paged_attn_decode_store) alone, `reps` times each way, HIP events on its stream:
+    warm (calls back to back, the previous call's K/V partly still in L2 and the Infinity Cache) and cold (1 GiB
+    of unrelated data written just before each call, outside the events, so the caches hold none of its K/V
+    and are full of dirty lines, as after a large GEMM). Medians in microseconds, and fractions of HBM peak."""
     flush = torch.empty(2**30 // 4, dtype=torch.int32, device=runner.q.device)
     out = {}
     for mode in ("warm", "cold"):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
-        runner.attention_only()
+        runner.fused_only()
         for i, e in enumerate(ev):
             if mode == "cold":
                 flush.fill_(i)
             e[0].record()
-            runner.attention_only()
+            runner.fused_only()
             e[1].record()
         torch.cuda.synchronize()
-        out[mode] = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+        us = float(np.median([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+        out[mode] = us
+        out[mode + "_frac"] = call_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS
     del flush
     return out
 
@@ -663,7 +673,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the 28-layer scheduler-trace replay")
-    ap.add_argument("--no-fused", action="store_true", help="skip the decode step with the store fused")
+    ap.add_argument("--no-fused", action="store_true", help="skip the decode step as two calls (store, attention)")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode (512 seqs, 4K-32K tokens)")
     ap.add_argument("--no-back-to-back", action="store_true",
                     help="skip the 0.1 s back-to-back prefill run (keeps a kernel trace to the timed steps)")
@@ -686,32 +696,35 @@ def main():
     log(f"[bench] device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
         f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
 
-    # ---- decode step ----
+    # ---- decode step (headline): prepare + upload + paged_attn_decode_store ----
     log("[bench] decode workload: setup stores ...")
     dw = H.DeviceWorkload(wd, dev)
     dw.run_setup()
     torch.cuda.synchronize()
     runner = H.StepRunner(dw, wd.passes[0])
-    ms, store_ms, attn_ms = time_steps(runner, args.steps, args.warmup, torch)
     db = decode_bytes(wd)
     step_bytes = db["attn"] + db["store"]
+    ms, call_ms = fused_steps(runner, args.steps, args.warmup, torch)
     value = step_bytes / (ms * 1e-3) / 1e9
-    attn_avg = float(attn_ms.mean())
-    achieved = db["attn"] / (attn_avg * 1e-3) / 1e9
-    log(f"[bench] decode step {ms * 1e3:.1f} us wall; store {store_ms.mean() * 1e3:.1f} us, "
-        f"attention {attn_avg * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
-    cw = cold_warm(torch, runner)
-    log(f"[bench] decode attention, median of 50: warm {cw['warm']:.1f} us "
-        f"({db['attn'] / (cw['warm'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%}), cold (1 GiB written before each call) "
-        f"{cw['cold']:.1f} us ({db['attn'] / (cw['cold'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%})")
-    fused = None
+    call_avg = float(call_ms.mean())
+    achieved = db["fused_call"] / (call_avg * 1e-3) / 1e9
+    log(f"[bench] decode step {ms * 1e3:.1f} us wall -> {value:.0f} GB/s; paged_attn_decode_store call "
+        f"{call_avg * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
+    cw = cold_warm(torch, runner, db["fused_call"])
+    log(f"[bench] decode call, median of 50: warm {cw['warm']:.1f} us ({cw['warm_frac']:.1%}), cold (1 GiB written "
+        f"before each call) {cw['cold']:.1f} us ({cw['cold_frac']:.1%})")
+    two = None
     if not args.no_fused:
-        fms, fcall = fused_steps(runner, args.steps, args.warmup, torch)
-        fused = {"ms_per_step": round(fms, 5), "gbs": round(step_bytes / (fms * 1e-3) / 1e9, 1),
-                 "call_us": round(fcall * 1e3, 2),
-                 "note": "the same decode step with the store fused into the attention call "
-                         "(paged_attn_decode_store)"}
-        log(f"[bench] decode step with the store fused: {fms * 1e3:.1f} us wall; call {fcall * 1e3:.1f} us")
+        tms, store_ms, attn_ms = time_steps(runner, args.steps, args.warmup, torch)
+        attn_avg = float(attn_ms.mean())
+        two = {"ms_per_step": round(tms, 5), "gbs": round(step_bytes / (tms * 1e-3) / 1e9, 1),
+               "store_us": round(float(store_ms.mean()) * 1e3, 2), "attn_us": round(attn_avg * 1e3, 2),
+               "attn_gbs": round(db["attn"] / (attn_avg * 1e-3) / 1e9, 1),
+               "attn_frac_hbm_peak": round(db["attn"] / (attn_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               "note": "the same decode step as two calls: kv_store, then paged_attn_decode (HIP events around "
+                       "each on its stream)"}
+        log(f"[bench] decode step as two calls: {tms * 1e3:.1f} us wall; store {store_ms.mean() * 1e3:.1f} us, "
+            f"attention {attn_avg * 1e3:.1f} us ({two['attn_frac_hbm_peak']:.1%} of HBM peak)")
 
     # ---- prefill step ----
     prefill = None
@@ -744,6 +757,15 @@ def main():
             b2b_line = {"attn_us": round(b2b * 1e3, 2), "tflops": round(b2b_tflops, 2),
                         "pct_bf16_peak": round(100 * b2b_tflops / BF16_PEAK_TFLOPS, 2),
                         "note": "the same call launched back to back for 0.1 s after the timed steps"}
+        fpms, fpcall = fused_steps(rp, max(args.steps // 2, 5), args.warmup, torch)
+        fpav = float(fpcall.mean())
+        fused_line = {"step_us_wall": round(fpms * 1e3, 2), "call_us": round(fpav * 1e3, 2),
+                      "tflops": round(pw["flops"] / (fpav * 1e-3) / 1e12, 2),
+                      "pct_bf16_peak": round(100 * pw["flops"] / (fpav * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 2),
+                      "note": "the same step with the store fused into the prefill call (paged_attn_prefill_store): "
+                              "host prepare + upload + one call; TFLOP/s counts the attention flops only"}
+        log(f"[bench] prefill step with the store fused: {fpms * 1e3:.1f} us wall; call {fpav * 1e3:.1f} us "
+            f"({fused_line['tflops']:.1f} TFLOP/s of attention flops)")
         rope = rope_store_rate(torch, wp, rp, max(args.steps // 2, 5))
         prefill = {"workload": "chunked prefill: 36 seqs, 16124 new tokens (budget 16384), prompts U[100,1024], "
                                "about half with a shared 256/512-token cached prefix, first seq a mid-block chunk "
@@ -755,6 +777,7 @@ def main():
                    "t_mfma_us": round(t_mfma * 1e6, 2), "t_hbm_us": round(t_hbm * 1e6, 2),
                    "roofline_frac": round(roof, 4),
                    "back_to_back": b2b_line,
+                   "fused_store_step": fused_line,
                    "rope_kv_store": rope}
 
     long_dec = None if args.no_long else long_decode(torch, dev, max(args.steps // 5, 5), 3)
@@ -778,23 +801,20 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 q/k/v; no model weights)",
         "config": {"workload": "decode: 256 seqs + 16 padding rows (272), context U[100,2048], GQA 16Q/8KV, "
                                "head_dim 128, bf16, block 256, shuffled pool 1.25x; step = host prepare + upload "
-                               "+ kv_store + paged_attn_decode",
+                               "+ paged_attn_decode_store (kv_store of the new tokens fused into decode attention)",
                    "global_batch": 272, "seq_len": int(max(s.seq_len for s in wd.store.seqs)),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "paged_attn_decode call (decode_stream_kernel + decode_merge_kernel), HIP events "
-                               "on its stream, mean over the timed steps",
-                     "algorithmic_bytes": db["attn"], "us": round(attn_avg * 1e3, 2),
-                     "warm_median_us": round(cw["warm"], 2),
-                     "warm_median_frac": round(db["attn"] / (cw["warm"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "cold_median_us": round(cw["cold"], 2),
-                     "cold_median_frac": round(db["attn"] / (cw["cold"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel": "paged_attn_decode_store call (decode_stream_kernel with the store fused + "
+                               "decode_merge_kernel), HIP events on its stream, mean over the timed steps",
+                     "algorithmic_bytes": db["fused_call"], "us": round(call_avg * 1e3, 2),
+                     "warm_median_us": round(cw["warm"], 2), "warm_median_frac": round(cw["warm_frac"], 4),
+                     "cold_median_us": round(cw["cold"], 2), "cold_median_frac": round(cw["cold_frac"], 4),
                      "cold_note": "median of 50 calls, each after 1 GiB of unrelated data was written (outside the "
                                   "events): nothing of the call's K/V in L2 or the Infinity Cache; warm: 50 calls "
                                   "back to back"},
-        "decode_store_us": round(float(store_ms.mean()) * 1e3, 2),
-        "decode_step_fused": fused,
+        "decode_step_two_calls": two,
         "prefill": prefill,
         "long_decode": long_dec,
         "decode_graph": graph,

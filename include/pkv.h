@@ -60,7 +60,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 8
+#define PKV_ABI_VERSION 9
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -282,6 +282,43 @@ pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu
                                      int32_t block_size, int64_t num_blocks, float scale,
                                      const int32_t* work_items, int32_t num_work_items,
                                      void* stream);
+
+/*
+ * paged_attn_prefill_store — kv_store of the step's new tokens followed by
+ * paged_attn_prefill_varlen, in one launch (P1, "第六站：注意力层": each step
+ * stores the new tokens' K/V before attention reads the context through the
+ * block table). Results equal those two calls bit for bit: positions
+ * c_s .. L_s - 1 of sequence s (its query tokens) are read from the step's
+ * key/value rows cu_seqlens_q[s] .. cu_seqlens_q[s+1] - 1 instead of the
+ * cache, and the work-group that owns a query tile also writes that tile's
+ * K/V rows of its KV head to cache row slot_mapping[token]; no position of
+ * the call reads a row the call writes.
+ *
+ *   key, value       device bf16 [total_q, num_kv_heads, head_dim]; token t's
+ *                    row starts at key + t * key_token_stride elements
+ *                    (16-byte aligned rows; a strided view of a fused QKV
+ *                    buffer works; stride at most 2^25 elements)
+ *   slot_mapping     device int32 [total_q]: the cache row of each token
+ *                    (as pkv_prepare_step writes it); -1 or a slot outside
+ *                    the pool stores nothing
+ *   k_cache, v_cache written at the slots' rows and read elsewhere
+ *   other arguments  as for paged_attn_prefill_varlen (plan or grid launch)
+ * Errors: as for paged_attn_prefill_varlen, plus PKV_ERR_INVALID for null
+ * key/value/slot_mapping or a token stride below a row, and
+ * PKV_ERR_UNSUPPORTED for rows not 16-byte aligned or strides above 2^25.
+ * Slots that disagree with the block tables are the caller's error (the
+ * attention then uses the new rows while the cache receives them
+ * elsewhere).
+ */
+pkv_status paged_attn_prefill_store(void* out, const void* q, const void* key, int64_t key_token_stride,
+                                    const void* value, int64_t value_token_stride,
+                                    const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                    const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                    const int32_t* block_tables, int32_t block_table_stride, int32_t num_seqs,
+                                    int32_t total_q, int32_t max_q_len, int32_t max_context_len,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size, int64_t num_blocks, float scale,
+                                    const int32_t* work_items, int32_t num_work_items, void* stream);
 
 /*
  * pkv_prefill_plan — host-side work list for paged_attn_prefill_varlen.

@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     paged_attn_decode_noalloc,
     paged_attn_decode_workspace_size,
     paged_attn_prefill_varlen,
+    paged_attn_prefill_store,
     pkv_prefill_plan,
     pkv_prepare_step,
     pkv_rope_cos_sin,

@@ -22,12 +22,12 @@ STATUS = {0: "OK", 1: "INVALID", 2: "UNSUPPORTED", 3: "HIP", 4: "WORKSPACE"}
 EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
            "paged_attn_decode_workspace_size", "paged_attn_decode", "paged_attn_decode_noalloc",
            "paged_attn_decode_store",
-           "paged_attn_prefill_varlen",
+           "paged_attn_prefill_varlen", "paged_attn_prefill_store",
            "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
            "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks", "pkv_decode_graphs_create",
            "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy", "rope_kv_store", "pkv_rope_cos_sin",
            "sample_temperature_workspace_size", "sample_temperature")
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class PkvError(RuntimeError):
@@ -99,6 +99,10 @@ def load_library(path: str = LIB_PATH):
     lib.paged_attn_prefill_varlen.argtypes = [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32,
                                               c_i32, c_i32, c_i32, c_i32, c_i32, c_i64, c_f32, c_vp, c_i32,
                                               c_vp]
+    lib.paged_attn_prefill_store.restype = c_i32
+    lib.paged_attn_prefill_store.argtypes = [c_vp, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                             c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i64,
+                                             c_f32, c_vp, c_i32, c_vp]
     lib.pkv_prefill_plan.restype = c_i32
     lib.pkv_prefill_plan.argtypes = [c_i32, P_I32, P_I32, c_i32, c_i32, P_I32, c_i64, P_I64]
     lib.pkv_sched_create.restype = c_i32
@@ -589,6 +593,42 @@ def paged_attn_prefill_varlen(out, q, cu_seqlens_q, context_lens, k_cache, v_cac
                                        T, int(max_q_len), int(max_context_len), Hq, Hkv, D, B, N, float(scale),
                                        wi_ptr, int(wi_n), _stream(stream))
     _check("paged_attn_prefill_varlen", st)
+
+
+def paged_attn_prefill_store(out, q, key, value, slot_mapping, k_cache, v_cache, cu_seqlens_q, context_lens,
+                             block_tables, max_q_len, max_context_len, scale, work_items=None, stream=None):
+    """kv_store of the step's tokens and paged_attn_prefill_varlen in one call. key/value [T, H_kv, D] bf16 (token
+    stride may exceed a row); slot_mapping [T] int32; the rest as for paged_attn_prefill_varlen."""
+    torch = _torch()
+    lib = load_library()
+    T, Hq, D = q.shape
+    N, B, Hkv, _ = k_cache.shape
+    S = cu_seqlens_q.shape[0] - 1
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    if block_tables.dim() != 2 or block_tables.shape[0] < S or context_lens.shape[0] < S:
+        raise ValueError("block_tables / context_lens do not cover the batch")
+    if key.shape[0] < T or value.shape[0] < T or slot_mapping.shape[0] < T:
+        raise ValueError("key, value and slot_mapping must cover the step's tokens")
+    for t, n in ((key, "key"), (value, "value")):
+        if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise ValueError(f"{n} rows must be contiguous [H_kv, D]")
+    wi_ptr, wi_n = None, 0
+    if work_items is not None:
+        if work_items.dim() != 2 or work_items.shape[1] != 2:
+            raise ValueError("work_items must be [n, 2]")
+        wi_ptr, wi_n = _dev(work_items, "work_items", torch.int32), work_items.shape[0]
+    st = lib.paged_attn_prefill_store(_dev(out, "out", torch.bfloat16), _dev(q, "q", torch.bfloat16),
+                                      _dev(key, "key", torch.bfloat16, False), key.stride(0),
+                                      _dev(value, "value", torch.bfloat16, False), value.stride(0),
+                                      _dev(slot_mapping, "slot_mapping", torch.int32),
+                                      _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+                                      _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32),
+                                      _dev(context_lens, "context_lens", torch.int32),
+                                      _dev(block_tables, "block_tables", torch.int32), block_tables.stride(0), S, T,
+                                      int(max_q_len), int(max_context_len), Hq, Hkv, D, B, N, float(scale), wi_ptr,
+                                      int(wi_n), _stream(stream))
+    _check("paged_attn_prefill_store", st)
 
 
 class DecodeGraphs:

@@ -162,17 +162,86 @@ __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* _
 #pragma clang diagnostic pop
 }
 
-template <int G>
+// The step's new K/V rows for the fused store (paged_attn_prefill_store):
+// positions >= num_cached of a sequence are read from the step's key/value
+// input (token q0 + p - c of the step) instead of the cache, and each
+// work-group writes its own query tokens' rows of its KV head to their
+// slots. k == nullptr when the caller stored the rows beforehand.
+struct NewRows {
+  const char* k;
+  const char* v;
+  int64_t k_stride_b, v_stride_b;  // bytes between tokens
+  const int32_t* slots;            // the step's slot mapping, one slot per token
+  int64_t num_slots;               // rows in each cache
+  char* k_cache;                   // the caches, writable (only the slots' rows are written)
+  char* v_cache;
+};
+
+// issue_tile for a tile that holds new tokens: rows r < cut (positions < c)
+// from the cache (descriptor as in issue_tile), rows r >= cut from the
+// step's input rows, whose tile row r is at kin / vin + (r - rs) * stride
+// (rs = max(cut, 0), the first input row); input rows past the context end
+// load its last row. Chunks are swizzled as in issue_tile. A row's source is
+// chosen per 16-lane group with the exec mask, so each load writes only its
+// rows' LDS locations.
+__device__ __forceinline__ void issue_tile_new(char* kbuf, char* vbuf, const char* __restrict__ kc,
+                                               const char* __restrict__ vc, int32_t blk32, int key0, int L, int cut,
+                                               int64_t row_bytes, int64_t block_bytes, int head_off,
+                                               uint32_t num_blocks32, int wave, const uint32_t (&koff)[4],
+                                               const uint32_t (&voff)[4], const char* kin, const char* vin,
+                                               uint32_t ks, uint32_t vs) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane >> 4;
+  const int cp = lane & 15;
+  const int last = L - 1 - key0;  // >= cut: the context's last position is a new token
+  const int rs = cut > 0 ? cut : 0;
+  const __amdgpu_buffer_rsrc_t ki = __builtin_amdgcn_make_buffer_rsrc((void*)kin, (short)0, kKeysPerTile * ks, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vi = __builtin_amdgcn_make_buffer_rsrc((void*)vin, (short)0, kKeysPerTile * vs, 0x00020000);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+  if (cut > 0) {  // straddles the cached prefix: its first rows come from the cache
+    const int64_t blk = (uint32_t)blk32 < num_blocks32 ? (int64_t)(uint32_t)blk32 : 0;
+    const int64_t base = blk * block_bytes + (int64_t)(key0 & (kBlockSize - 1)) * row_bytes + head_off;
+    const int span = kKeysPerTile * (int)row_bytes;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + base), (short)0, span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + base), (short)0, span, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kRowsW / 4; ++i) {
+      const int r0 = kRowsW * wave + 4 * i;
+      if (r0 + sub < cut) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(kbuf + r0 * kRowBytes), 16, koff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vbuf + r0 * kRowBytes), 16, voff[i], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsW / 4; ++i) {
+    const int r0 = kRowsW * wave + 4 * i;
+    const int r = r0 + sub;
+    if (r >= cut) {
+      // input row of tile row r (rows past the context end: its last row), relative to the first input row
+      const uint32_t ri = (uint32_t)((r < last ? r : last) - rs);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ki, (lds_void*)(kbuf + r0 * kRowBytes), 16,
+                                               ri * ks + 16 * (cp ^ (r & 15)), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vi, (lds_void*)(vbuf + r0 * kRowBytes), 16,
+                                               ri * vs + 16 * (cp ^ ((4 * r) & 15)), 0, 0, 0);
+    }
+  }
+#pragma clang diagnostic pop
+}
+
+template <int G, bool FUSED>
 __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
     const int32_t* __restrict__ context_lens, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int bt_stride, int hq, int hkv, int64_t num_blocks,
-    float scale_log2, int max_q, int max_ctx, const int2* __restrict__ items, int num_seqs) {
+    float scale_log2, int max_q, int max_ctx, const int2* __restrict__ items, int num_seqs, const NewRows nr) {
   constexpr int kTokWG = 128 / G;  // query tokens per work-group
   constexpr int kTokW = 32 / G;    // per wavefront
   // K0 V0 K1 V1; after the last tile, the output staging (32 rows per wavefront)
   __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes > 4 * 32 * kRowBytes ? 4 * kTileBytes
                                                                                        : 4 * 32 * kRowBytes];
+  __shared__ int32_t own_slots[FUSED ? kTokWG : 1];  // fused store: the slots of this work-group's query tokens
 
   // work item: from the host plan (one per non-empty tile, heaviest first),
   // else from the grid (kv_head, seq, q-tile counted from the end)
@@ -255,8 +324,32 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
     }
   }
   const uint32_t nblk32 = num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)num_blocks;
-  issue_tile(smem, smem + kTileBytes, k_cache, v_cache, bt[0], 0, L, row_bytes, block_bytes, head_off, nblk32, wave,
-             gk, gv);
+  // fused store: the input row of position c (token q0 of the step), this KV head
+  const char* kin0 = nullptr;
+  const char* vin0 = nullptr;
+  uint32_t ks = 0, vs = 0;
+  if constexpr (FUSED) {
+    kin0 = nr.k + (int64_t)q0 * nr.k_stride_b + head_off;
+    vin0 = nr.v + (int64_t)q0 * nr.v_stride_b + head_off;
+    ks = (uint32_t)nr.k_stride_b;
+    vs = (uint32_t)nr.v_stride_b;
+  }
+  int32_t my_slot = -1;  // fused store: loaded before the first tile is issued, kept in LDS after
+  if (FUSED && (int)threadIdx.x < tok_end - tok_begin) my_slot = nr.slots[q0 + tok_begin + threadIdx.x];
+  // K/V of the tile starting at key0: from the cache, or (fused store) partly or wholly from the input rows
+  auto issue = [&](char* kb, int key0, int32_t blk32) {
+    if (!FUSED || key0 + kKeysPerTile <= c) {
+      issue_tile(kb, kb + kTileBytes, k_cache, v_cache, blk32, key0, L, row_bytes, block_bytes, head_off, nblk32,
+                 wave, gk, gv);
+    } else {
+      const int cut = c - key0;
+      const int64_t first = key0 > c ? key0 - c : 0;  // input row of the tile's first new token
+      issue_tile_new(kb, kb + kTileBytes, k_cache, v_cache, blk32, key0, L, cut, row_bytes, block_bytes, head_off,
+                     nblk32, wave, gk, gv, kin0 + first * nr.k_stride_b, vin0 + first * nr.v_stride_b, ks, vs);
+    }
+  };
+  issue(smem, 0, bt[0]);
+  if (FUSED && (int)threadIdx.x < tok_end - tok_begin) own_slots[threadIdx.x] = my_slot;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) retire(qreg[kk]);
   __builtin_amdgcn_s_waitcnt(0);
@@ -283,15 +376,40 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
   // addresses fold the stage base into the instructions' offset fields
   auto key_tile = [&](auto stage_c, const int kt) {
     constexpr int stg = decltype(stage_c)::value;
-    const bool has_next = kt + 1 < nkt;
-    if (has_next) {
-      char* nb = smem + (1 - stg) * 2 * kTileBytes;
-      issue_tile(nb, nb + kTileBytes, k_cache, v_cache, bt[((kt + 1) * kKeysPerTile) >> 8], (kt + 1) * kKeysPerTile,
-                 L, row_bytes, block_bytes, head_off, nblk32, wave, gk, gv);
-    }
     const char* kbuf = smem + stg * 2 * kTileBytes;
     const char* vbuf = kbuf + kTileBytes;
     const int key0 = kt * kKeysPerTile;
+    if constexpr (FUSED) {
+      // Fused store: this tile's rows of the work-group's own query tokens (positions c + tok_begin ..
+      // c + tok_end - 1, read from the input into LDS) go to their slots, head g only; each (token, KV head)
+      // belongs to exactly one work-group. Issued before the next tile's loads, so the end-of-tile wait
+      // covers these stores too.
+      const int own_lo = c + tok_begin - key0 > 0 ? c + tok_begin - key0 : 0;
+      const int own_hi = c + tok_end - key0 < kKeysPerTile ? c + tok_end - key0 : kKeysPerTile;
+      if (own_lo < own_hi) {
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));  // keeps the address arithmetic here (hoisted, it would be spilled)
+        const int row = tid >> 3;
+        const int j = tid & 7;
+        if (row >= own_lo && row < own_hi) {
+          const int32_t slot = own_slots[key0 + row - c - tok_begin];
+          if (slot >= 0 && (int64_t)slot < nr.num_slots) {
+            char* kd = nr.k_cache + (int64_t)slot * row_bytes + head_off;
+            char* vd = nr.v_cache + (int64_t)slot * row_bytes + head_off;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int ch = 2 * j + h;  // logical 16-byte chunk
+              *reinterpret_cast<u32x4*>(kd + 16 * ch) =
+                  *reinterpret_cast<const u32x4*>(kbuf + row * kRowBytes + 16 * (ch ^ (row & 15)));
+              *reinterpret_cast<u32x4*>(vd + 16 * ch) =
+                  *reinterpret_cast<const u32x4*>(vbuf + row * kRowBytes + 16 * (ch ^ ((4 * row) & 15)));
+            }
+          }
+        }
+      }
+    }
+    const bool has_next = kt + 1 < nkt;
+    if (has_next) issue(smem + (1 - stg) * 2 * kTileBytes, (kt + 1) * kKeysPerTile, bt[((kt + 1) * kKeysPerTile) >> 8]);
     const bool act0 = wave_live && key0 <= pmax;
     const bool act1 = kSub == 2 && wave_live && key0 + 32 <= pmax;
     if (act0) {
@@ -451,15 +569,15 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
 
 }  // namespace pkv
 
-extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,
-                                                const int32_t* context_lens, const void* k_cache,
-                                                const void* v_cache, const int32_t* block_tables,
-                                                int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
-                                                int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
-                                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                                int64_t num_blocks, float scale, const int32_t* work_items,
-                                                int32_t num_work_items, void* stream) {
-  using namespace pkv;
+namespace pkv {
+namespace {
+
+pkv_status prefill_call(void* out, const void* q, const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        int32_t block_table_stride, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                        int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int64_t num_blocks, float scale, const int32_t* work_items,
+                        int32_t num_work_items, void* stream, const NewRows& nr) {
   if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_context_len < 0 || num_blocks < 0 ||
       block_table_stride < 0)
     return fail(PKV_ERR_INVALID, "paged_attn_prefill_varlen: negative size");
@@ -501,16 +619,74 @@ extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const 
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const char* kc = static_cast<const char*>(k_cache);
   const char* vc = static_cast<const char*>(v_cache);
-#define PKV_PREFILL_LAUNCH(GG)                                                                                  \
-  hipLaunchKernelGGL(prefill_kernel<GG>, grid, dim3(256), 0, s, o, qq, cu_seqlens_q, context_lens, kc, vc,      \
-                     block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2,      \
-                     max_q_len, max_context_len, items, num_seqs)
-  switch (G) {
-    case 1: PKV_PREFILL_LAUNCH(1); break;
-    case 2: PKV_PREFILL_LAUNCH(2); break;
-    case 4: PKV_PREFILL_LAUNCH(4); break;
-    default: PKV_PREFILL_LAUNCH(8); break;
+#define PKV_PREFILL_LAUNCH(GG, FF)                                                                               \
+  hipLaunchKernelGGL((prefill_kernel<GG, FF>), grid, dim3(256), 0, s, o, qq, cu_seqlens_q, context_lens, kc, vc, \
+                     block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2,       \
+                     max_q_len, max_context_len, items, num_seqs, nr)
+#define PKV_PREFILL_G(FF)                  \
+  switch (G) {                             \
+    case 1: PKV_PREFILL_LAUNCH(1, FF); break; \
+    case 2: PKV_PREFILL_LAUNCH(2, FF); break; \
+    case 4: PKV_PREFILL_LAUNCH(4, FF); break; \
+    default: PKV_PREFILL_LAUNCH(8, FF); break; \
   }
+  if (nr.k) {
+    PKV_PREFILL_G(true)
+  } else {
+    PKV_PREFILL_G(false)
+  }
+#undef PKV_PREFILL_G
 #undef PKV_PREFILL_LAUNCH
   return check_launch("paged_attn_prefill_varlen");
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,
+                                                const int32_t* context_lens, const void* k_cache,
+                                                const void* v_cache, const int32_t* block_tables,
+                                                int32_t block_table_stride, int32_t num_seqs, int32_t total_q,
+                                                int32_t max_q_len, int32_t max_context_len, int32_t num_q_heads,
+                                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                int64_t num_blocks, float scale, const int32_t* work_items,
+                                                int32_t num_work_items, void* stream) {
+  const pkv::NewRows none{nullptr, nullptr, 0, 0, nullptr, 0, nullptr, nullptr};
+  return pkv::prefill_call(out, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables, block_table_stride,
+                           num_seqs, total_q, max_q_len, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                           block_size, num_blocks, scale, work_items, num_work_items, stream, none);
+}
+
+extern "C" pkv_status paged_attn_prefill_store(void* out, const void* q, const void* key, int64_t key_token_stride,
+                                               const void* value, int64_t value_token_stride,
+                                               const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                               const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                               const int32_t* block_tables, int32_t block_table_stride,
+                                               int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                               int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                               float scale, const int32_t* work_items, int32_t num_work_items,
+                                               void* stream) {
+  using namespace pkv;
+  if (num_seqs > 0 && total_q > 0) {
+    if (!key || !value || !slot_mapping) return fail(PKV_ERR_INVALID, "paged_attn_prefill_store: null pointer");
+    if (head_dim != kHeadDim)
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_store: head_dim %d (128 only)", head_dim);
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (key_token_stride < row || value_token_stride < row)
+      return fail(PKV_ERR_INVALID, "paged_attn_prefill_store: token stride smaller than a row (%lld elements)",
+                  (long long)row);
+    if ((key_token_stride * 2) % 16 || (value_token_stride * 2) % 16 || !aligned16(key) || !aligned16(value))
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_store: key/value and their strides must be 16-byte aligned");
+    if (key_token_stride > (1 << 25) || value_token_stride > (1 << 25))
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_prefill_store: token stride above 2^25 elements");
+    if (num_blocks > INT64_MAX / kBlockSize)
+      return fail(PKV_ERR_INVALID, "paged_attn_prefill_store: num_blocks out of range");
+  }
+  const NewRows nr{static_cast<const char*>(key), static_cast<const char*>(value), key_token_stride * 2,
+                   value_token_stride * 2, slot_mapping, num_blocks * kBlockSize, static_cast<char*>(k_cache),
+                   static_cast<char*>(v_cache)};
+  return prefill_call(out, q, cu_seqlens_q, context_lens, k_cache, v_cache, block_tables, block_table_stride,
+                      num_seqs, total_q, max_q_len, max_context_len, num_q_heads, num_kv_heads, head_dim, block_size,
+                      num_blocks, scale, work_items, num_work_items, stream, nr);
 }

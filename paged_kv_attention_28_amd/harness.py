@@ -158,18 +158,28 @@ class StepRunner:
                                          flat[offs[5]:offs[6]]))
         self.i = 0
 
-    def prepare_and_upload(self):
+    def prepare_and_upload(self, record_guard: bool = True) -> int:
         """Host step preparation (pkv_prepare_step, plus pkv_prefill_plan for a
-        prefill step) into the next pinned buffer set, then one upload."""
+        prefill step) into the next pinned buffer set, then one upload.
+        Returns the buffer set used. With record_guard=False the caller
+        records, after this step's work, the event that guards the set's
+        reuse (``guard(k, event)``), so the step enqueues no extra marker."""
         k = self.i & 1
         self.i += 1
         if self.events[k] is not None:
             self.events[k].synchronize()
         _, self.num_items = self.preps[k]()
         self.dev_flat.copy_(self.pinned[k], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record()
-        self.events[k] = ev
+        self.events[k] = None
+        if record_guard:
+            ev = torch.cuda.Event()
+            ev.record()
+            self.events[k] = ev
+        return k
+
+    def guard(self, k: int, event):
+        """An event recorded after buffer set k's upload guards its reuse."""
+        self.events[k] = event
 
     def store_only(self):
         slots = self.dev_meta[0]
@@ -188,12 +198,17 @@ class StepRunner:
                                         self.max_q_len, self.max_ctx, w.scale, work_items=items)
 
     def fused_only(self):
-        """Decode passes: the store and the attention in one call (paged_attn_decode_store)."""
+        """The store and the attention in one call (paged_attn_decode_store, paged_attn_prefill_store)."""
         w = self.dw.w
-        slots, _, ctx, bt = self.dev_meta
+        slots, cu, ctx, bt = self.dev_meta
         bt2 = bt.view(-1, w.max_blocks_per_seq)
-        B.paged_attn_decode_store(self.out, self.q, self.k, self.v, slots, self.dw.k_cache, self.dw.v_cache, bt2, ctx,
-                                  w.scale, self.max_ctx, self.workspace)
+        if self.p.kind == "decode":
+            B.paged_attn_decode_store(self.out, self.q, self.k, self.v, slots, self.dw.k_cache, self.dw.v_cache, bt2,
+                                      ctx, w.scale, self.max_ctx, self.workspace)
+        else:
+            items = self.dev_plan[:2 * self.num_items].view(self.num_items, 2)
+            B.paged_attn_prefill_store(self.out, self.q, self.k, self.v, slots, self.dw.k_cache, self.dw.v_cache, cu,
+                                       ctx, bt2, self.max_q_len, self.max_ctx, w.scale, work_items=items)
 
     def kernels(self):
         self.store_only()

@@ -322,6 +322,55 @@ def test_decode_store_fused_matches_two_calls(case):
     assert np.array_equal(_cache_bits(dw.v_cache), va), f"{case}: V cache differs"
 
 
+PREFILL_FUSED_CASES = ["config3", "prefill_single_tokens", "prefill_ragged", "prefill_gqa1", "prefill_gqa4",
+                       "prefill_gqa8", "prefill_long_prefix", "prefill_hkv1", "prefill_hq64", "prefill_long_ctx",
+                       "prefill_peaky", "prefill_ramp_gqa4", "prefill_hkv4_gqa2", "prefill_hkv4_gqa4"]
+
+
+@pytest.mark.parametrize("case", PREFILL_FUSED_CASES)
+@pytest.mark.parametrize("layout", ["rows", "qkv_view"])
+def test_prefill_store_fused_matches_two_calls(case, layout):
+    """paged_attn_prefill_store (new tokens read from their input rows, each query tile's rows stored by the
+    work-group that owns the tile) gives the bits of kv_store followed by paged_attn_prefill_varlen: outputs and
+    both caches, on the plan and on the full grid. layout qkv_view passes key and value as strided views of one
+    [tokens, (H_q + 2 H_kv) x 128] buffer, as a fused QKV projection writes them."""
+    from paged_kv_attention_28_amd import binding as B
+    w = W.make(3) if case == "config3" else custom(**EDGE[case])
+    p = w.passes[0]
+    dw = H.DeviceWorkload(w)
+    dw.run_setup()
+    k0, v0 = dw.k_cache.clone(), dw.v_cache.clone()
+    key, value = W.store_kv(w, "cuda")
+    slots = dw.store_slots()
+    q, m = dw.pass_inputs(p)
+    T, hkv = key.shape[0], w.num_kv_heads
+    if layout == "qkv_view":
+        width = (w.num_q_heads + 2 * hkv) * 128
+        buf = torch.zeros(T, width, dtype=torch.bfloat16, device="cuda")
+        buf[:, w.num_q_heads * 128:(w.num_q_heads + hkv) * 128] = key.reshape(T, -1)
+        buf[:, (w.num_q_heads + hkv) * 128:] = value.reshape(T, -1)
+        key = buf[:, w.num_q_heads * 128:].as_strided((T, hkv, 128), (width, 128, 1))
+        value = buf[:, (w.num_q_heads + hkv) * 128:].as_strided((T, hkv, 128), (width, 128, 1))
+    print(f"[fused prefill] {case} {layout}: {T} tokens, {len(p.batch.seqs)} sequences", flush=True)
+    B.kv_store(key, value, dw.k_cache, dw.v_cache, slots)
+    ref = torch.empty_like(q)
+    B.paged_attn_prefill_varlen(ref, q, m.cu_seqlens_q, m.context_lens, dw.k_cache, dw.v_cache, m.block_tables,
+                                m.max_q_len, m.max_context_len, w.scale, work_items=m.work_items)
+    torch.cuda.synchronize()
+    ka, va = _cache_bits(dw.k_cache), _cache_bits(dw.v_cache)
+    for plan in (True, False):
+        dw.k_cache.copy_(k0)
+        dw.v_cache.copy_(v0)
+        out = torch.full_like(q, float("nan"))
+        B.paged_attn_prefill_store(out, q, key, value, slots, dw.k_cache, dw.v_cache, m.cu_seqlens_q, m.context_lens,
+                                   m.block_tables, m.max_q_len, m.max_context_len, w.scale,
+                                   work_items=m.work_items if plan else None)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"{case} plan={plan}: outputs differ"
+        assert np.array_equal(_cache_bits(dw.k_cache), ka), f"{case} plan={plan}: K cache differs"
+        assert np.array_equal(_cache_bits(dw.v_cache), va), f"{case} plan={plan}: V cache differs"
+
+
 def test_prefill_long_prompt_sampled():
     """One 16384-token prompt (the whole token budget in one sequence: 256 query tiles, 64 blocks), launched on
     the plan and on the full grid: sampled rows against the oracle, each row computed by the oracle's decode
