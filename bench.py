@@ -601,44 +601,45 @@ def long_decode(torch, dev, steps: int, warmup: int) -> dict:
     return out
 
 
-def graph_vs_eager(torch, dev, iters: int = 200):
-    """Host-side cost of a decode step (store + attention) issued eagerly
-    through the binding versus replayed from a captured graph, on decode
-    batches shaped like the scheduler replay's (contexts U[100, 1024]),
-    where launch overhead matters most."""
+def graph_vs_eager(torch, dev, iters: int = 50, num_layers: int = 28):
+    """A model's whole decode step, every layer's store + attention (28 layers of 16 Q / 8 KV x 128, each with
+    its own caches), issued eagerly through the binding (one paged_attn_decode_store call per layer) versus
+    replayed from one captured graph per bucket holding all layers (pkv_decode_graphs_create_layers), on
+    batches shaped like the scheduler replay's (contexts U[100, 1024]). Wall-clock per step over back-to-back
+    steps."""
     from paged_kv_attention_28_amd import binding as B
     rng = np.random.default_rng(7)
     rows, mb, hq, hkv, d = 256, 4, 16, 8, 128
     lens = rng.integers(100, 1025, size=rows).astype(np.int32)
     nblk = rows * mb
-    kc = torch.randn(nblk, 256, hkv, d, device=dev).to(torch.bfloat16)
-    vc = torch.randn_like(kc)
     bt_h = np.arange(nblk, dtype=np.int32).reshape(rows, mb)
     pos = lens - 1
     slots_h = (bt_h[np.arange(rows), pos // 256] * 256 + pos % 256).astype(np.int32)
     bt = torch.from_numpy(bt_h).to(dev)
     ctx = torch.from_numpy(lens).to(dev)
     slots = torch.from_numpy(slots_h).to(dev)
-    key = torch.randn(rows, hkv, d, device=dev).to(torch.bfloat16)
-    value = torch.randn_like(key)
-    q = torch.randn(rows, hq, d, device=dev).to(torch.bfloat16)
-    out = torch.empty_like(q)
+    layers = []
+    for _ in range(num_layers):
+        kc = torch.randn(nblk, 256, hkv, d, device=dev).to(torch.bfloat16)
+        layers.append(dict(kc=kc, vc=torch.randn_like(kc),
+                           key=torch.randn(rows, hkv, d, device=dev).to(torch.bfloat16),
+                           value=torch.randn(rows, hkv, d, device=dev).to(torch.bfloat16),
+                           q=torch.randn(rows, hq, d, device=dev).to(torch.bfloat16),
+                           out=torch.empty(rows, hq, d, device=dev).to(torch.bfloat16)))
     max_ctx = mb * 256
     ws = torch.empty(B.paged_attn_decode_workspace_size(rows, hq, hkv, d, max_ctx), dtype=torch.uint8, device=dev)
     buckets = [1, 2, 4, 8] + list(range(16, rows + 1, 16))
-    graphs = B.DecodeGraphs(key, value, slots, kc, vc, q, out, bt, ctx, ws, 1.0 / np.sqrt(d), max_ctx, buckets)
     scale = 1.0 / float(np.sqrt(d))
+    L0 = layers[0]
+    graphs = B.DecodeGraphs(L0["key"], L0["value"], slots, L0["kc"], L0["vc"], L0["q"], L0["out"], bt, ctx, ws, scale,
+                            max_ctx, buckets,
+                            layers=[(x["key"], x["value"], x["kc"], x["vc"], x["q"], x["out"]) for x in layers[1:]])
     res = []
     for batch in (1, 16, 64, 256):
-        views = (key[:batch], value[:batch], slots[:batch], q[:batch], out[:batch], bt[:batch], ctx[:batch])
-
         def eager():
-            B.kv_store(views[0], views[1], kc, vc, views[2])
-            B.paged_attn_decode(views[4], views[3], kc, vc, views[5], views[6], scale, max_ctx, ws)
-
-        def eager_fused():
-            B.paged_attn_decode_store(views[4], views[3], views[0], views[1], views[2], kc, vc, views[5], views[6],
-                                      scale, max_ctx, ws)
+            for x in layers:
+                B.paged_attn_decode_store(x["out"][:batch], x["q"][:batch], x["key"][:batch], x["value"][:batch],
+                                          slots[:batch], x["kc"], x["vc"], bt[:batch], ctx[:batch], scale, max_ctx, ws)
 
         def per_step(f):
             t0 = time.perf_counter()
@@ -648,20 +649,91 @@ def graph_vs_eager(torch, dev, iters: int = 200):
             return (time.perf_counter() - t0) / iters * 1e6
 
         launch = lambda: graphs.launch(batch)  # noqa: E731
-        for f in (eager, eager_fused, launch):
-            for _ in range(10):
+        for f in (eager, launch):
+            for _ in range(5):
                 f()
         torch.cuda.synchronize()
-        t_e, t_f, t_g = per_step(eager), per_step(eager_fused), per_step(launch)
-        res.append({"batch": batch, "bucket": min(b for b in buckets if b >= batch), "eager_us": round(t_e, 2),
-                    "eager_fused_us": round(t_f, 2), "graph_us": round(t_g, 2)})
-        log(f"[bench] decode step batch {batch}: eager {t_e:.1f} us (fused call {t_f:.1f} us), graph {t_g:.1f} us")
+        t_e, t_g = per_step(eager), per_step(launch)
+        res.append({"batch": batch, "bucket": min(b for b in buckets if b >= batch), "eager_us": round(t_e, 1),
+                    "graph_us": round(t_g, 1), "graph_speedup": round(t_e / t_g, 3)})
+        log(f"[bench] {num_layers}-layer decode step, batch {batch}: eager {t_e:.1f} us, graph {t_g:.1f} us "
+            f"({t_e / t_g:.2f}x)")
     graphs.close()
-    return {"workload": "decode steps (kv_store + paged_attn_decode) of 1/16/64/256 sequences, contexts U[100,1024], "
-                        "16Q/8KV, d128; wall-clock per step over back-to-back steps: eager calls through the binding "
-                        "(two calls, and the fused paged_attn_decode_store) vs graph replay of the smallest bucket "
-                        "(the fused call captured)",
+    del layers
+    torch.cuda.empty_cache()
+    return {"workload": f"one decode step of {num_layers} layers (16Q/8KV, d128, each layer its own caches; store "
+                        "fused into decode) for 1/16/64/256 sequences, contexts U[100,1024]; wall-clock per step over "
+                        f"{iters} back-to-back steps: {num_layers} eager paged_attn_decode_store calls through the "
+                        "binding vs one graph replay holding all layers (pkv_decode_graphs_create_layers)",
             "batches": res}
+
+
+def trace_small_batch_graphs(torch, max_rows: int = 64) -> dict:
+    """The scheduler-trace replay's small decode steps (at most `max_rows` rows, the tail where requests
+    finish), every layer, both ways on the same static buffers: eager (one paged_attn_decode_store call per
+    layer through the binding) and one graph replay per step holding all 28 layers. Each step's q/k/v are drawn
+    into the buffers before the timed region; HIP events bracket the step's launches."""
+    from workloads import sched as S
+    from paged_kv_attention_28_amd import binding as B
+    from paged_kv_attention_28_amd import harness as H
+    prompts, outputs = S.requests()
+    steps = B.Scheduler(S.POOL_BLOCKS, W.BLOCK_SIZE, S.MAX_NUM_SEQS, S.MAX_BATCHED_TOKENS).run(prompts, outputs)
+    small = [(i, st) for i, st in enumerate(steps) if st.kind == "decode" and len(st.seq_lens) + st.num_pad <= max_rows]
+    runner = H.TraceRunner(W.SEEDS[5], S.NUM_LAYERS, S.POOL_BLOCKS)
+    dev, hq, hkv, d, mb = runner.device, runner.hq, runner.hkv, runner.d, runner.mb
+    max_ctx = mb * W.BLOCK_SIZE
+    slots = torch.full((max_rows,), -1, dtype=torch.int32, device=dev)
+    bt = torch.full((max_rows, mb), -1, dtype=torch.int32, device=dev)
+    ctx = torch.zeros(max_rows, dtype=torch.int32, device=dev)
+    bufs = [dict(key=torch.zeros(max_rows, hkv, d, dtype=torch.bfloat16, device=dev),
+                 value=torch.zeros(max_rows, hkv, d, dtype=torch.bfloat16, device=dev),
+                 q=torch.zeros(max_rows, hq, d, dtype=torch.bfloat16, device=dev),
+                 out=torch.empty(max_rows, hq, d, dtype=torch.bfloat16, device=dev)) for _ in range(runner.L)]
+    ws = torch.empty(B.paged_attn_decode_workspace_size(max_rows, hq, hkv, d, max_ctx), dtype=torch.uint8, device=dev)
+    buckets = [b for b in [1, 2, 4, 8] + list(range(16, 513, 16)) if b <= max_rows]
+    b0 = bufs[0]
+    kc0, vc0 = runner.caches[0]
+    graphs = B.DecodeGraphs(b0["key"], b0["value"], slots, kc0, vc0, b0["q"], b0["out"], bt, ctx, ws, runner.scale,
+                            max_ctx, buckets,
+                            layers=[(b["key"], b["value"], kc, vc, b["q"], b["out"])
+                                    for b, (kc, vc) in zip(bufs[1:], runner.caches[1:])])
+    t = {"eager": 0.0, "graph": 0.0}
+    tokens = 0
+    for i, st in small:
+        m = B.pkv_prepare_step(st.seq_lens, st.num_cached, st.block_tables, W.BLOCK_SIZE, mb, st.num_pad)
+        rows = m.num_tokens
+        slots[:rows] = torch.from_numpy(np.ascontiguousarray(m.slot_mapping)).to(dev)
+        ctx[:rows] = torch.from_numpy(np.ascontiguousarray(m.context_lens)).to(dev)
+        bt[:rows] = torch.from_numpy(np.ascontiguousarray(m.block_tables)).to(dev)
+        for layer, b in enumerate(bufs):
+            q, k, v = runner.values(i, layer, rows)
+            b["q"][:rows], b["key"][:rows], b["value"][:rows] = q, k, v
+        for mode in ("eager", "graph"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            if mode == "eager":
+                for b, (kc, vc) in zip(bufs, runner.caches):
+                    B.paged_attn_decode_store(b["out"][:rows], b["q"][:rows], b["key"][:rows], b["value"][:rows],
+                                              slots[:rows], kc, vc, bt[:rows], ctx[:rows], runner.scale, max_ctx, ws)
+            else:
+                graphs.launch(rows)
+            e1.record()
+            torch.cuda.synchronize()
+            t[mode] += e0.elapsed_time(e1) * 1e3
+        tokens += len(st.seq_lens)
+    graphs.close()
+    del runner, bufs
+    torch.cuda.empty_cache()
+    out = {"steps": len(small), "max_rows": max_rows, "generated_tokens": tokens,
+           "eager_us": round(t["eager"], 1), "graph_us": round(t["graph"], 1),
+           "eager_tok_s": round(tokens / (t["eager"] * 1e-6), 1), "graph_tok_s": round(tokens / (t["graph"] * 1e-6), 1),
+           "note": f"decode steps of at most {max_rows} rows of the 28-layer scheduler trace; per step, HIP events "
+                   "around all layers' launches (28 eager calls, or one replay of the step's graph), q/k/v drawn "
+                   "before; both on the same static buffers"}
+    log(f"[bench] trace small decode steps ({len(small)} steps of <= {max_rows} rows, 28 layers): eager "
+        f"{t['eager'] / 1e3:.1f} ms -> {out['eager_tok_s']:.0f} tok/s, graph {t['graph'] / 1e3:.1f} ms -> "
+        f"{out['graph_tok_s']:.0f} tok/s")
+    return out
 
 
 def main():
@@ -784,6 +856,8 @@ def main():
     graph = None if args.no_graph else graph_vs_eager(torch, dev)
     sampler = sampler_rate(torch, dev)
     trace = None if args.no_trace else trace_replay(torch)
+    if trace is not None and not args.no_graph:
+        trace["small_decode_steps_graph_vs_eager"] = trace_small_batch_graphs(torch)
     copy = copy_ceiling(torch, dev)
 
     line = {

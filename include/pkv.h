@@ -60,7 +60,7 @@ const char* pkv_last_error(void);
 
 /* ABI revision of this header; bumped on any signature change. */
 int32_t pkv_abi_version(void);
-#define PKV_ABI_VERSION 9
+#define PKV_ABI_VERSION 10
 
 /*
  * pkv_prepare_step — per-step attention metadata, built on the host.
@@ -470,6 +470,17 @@ typedef struct pkv_decode_graphs pkv_decode_graphs;
  * PKV_ERR_HIP if capture or instantiation fails. The caller owns *out. */
 pkv_status pkv_decode_graphs_create(const pkv_decode_graph_desc* desc, const int32_t* buckets,
                                     int32_t num_buckets, pkv_decode_graphs** out);
+
+/* The same for a whole decode step of a model: each graph holds, in order,
+ * the call of every descriptor in layers[0 .. num_layers) (one per attention
+ * layer: its caches, q, out, key and value rows; the metadata buffers may be
+ * shared), so one replay runs all layers' stores and attention (P1, "第五站":
+ * the whole decode step is captured per bucket). pkv_decode_graphs_create
+ * is this call with one layer. A shared workspace is fine: the calls of one
+ * replay run one after another on the replay's stream. */
+pkv_status pkv_decode_graphs_create_layers(const pkv_decode_graph_desc* layers, int32_t num_layers,
+                                           const int32_t* buckets, int32_t num_buckets,
+                                           pkv_decode_graphs** out);
 
 /* Replay the smallest bucket >= batch on `stream`; *out_bucket (if non-NULL)
  * gets that bucket. PKV_ERR_INVALID if batch is outside [1, largest bucket]. */

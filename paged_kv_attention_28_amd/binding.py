@@ -25,9 +25,10 @@ EXPORTS = ("pkv_last_error", "pkv_abi_version", "pkv_prepare_step", "kv_store",
            "paged_attn_prefill_varlen", "paged_attn_prefill_store",
            "pkv_prefill_plan", "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add", "pkv_sched_schedule",
            "pkv_sched_postprocess", "pkv_sched_unfinished", "pkv_sched_free_blocks", "pkv_decode_graphs_create",
+           "pkv_decode_graphs_create_layers",
            "pkv_decode_graphs_launch", "pkv_decode_graphs_destroy", "rope_kv_store", "pkv_rope_cos_sin",
            "sample_temperature_workspace_size", "sample_temperature")
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class PkvError(RuntimeError):
@@ -121,6 +122,9 @@ def load_library(path: str = LIB_PATH):
     lib.pkv_sched_free_blocks.argtypes = [c_vp]
     lib.pkv_decode_graphs_create.restype = c_i32
     lib.pkv_decode_graphs_create.argtypes = [ctypes.POINTER(DecodeGraphDesc), P_I32, c_i32, ctypes.POINTER(c_vp)]
+    lib.pkv_decode_graphs_create_layers.restype = c_i32
+    lib.pkv_decode_graphs_create_layers.argtypes = [ctypes.POINTER(DecodeGraphDesc), c_i32, P_I32, c_i32,
+                                                    ctypes.POINTER(c_vp)]
     lib.pkv_decode_graphs_launch.restype = c_i32
     lib.pkv_decode_graphs_launch.argtypes = [c_vp, c_i32, P_I32, c_vp]
     lib.pkv_decode_graphs_destroy.restype = c_i32
@@ -631,49 +635,63 @@ def paged_attn_prefill_store(out, q, key, value, slot_mapping, k_cache, v_cache,
     _check("paged_attn_prefill_store", st)
 
 
+def _graph_desc(key, value, slot_mapping, k_cache, v_cache, q, out, block_tables, context_lens, workspace, scale,
+                max_context_len, rows):
+    torch = _torch()
+    N, B, Hkv, D = k_cache.shape
+    d = DecodeGraphDesc()
+    d.key = _dev(key, "key", torch.bfloat16, False)
+    d.key_stride = key.stride(0)
+    d.value = _dev(value, "value", torch.bfloat16, False)
+    d.value_stride = value.stride(0)
+    d.slot_mapping = _dev(slot_mapping, "slot_mapping", torch.int32)
+    d.k_cache = _dev(k_cache, "k_cache", torch.bfloat16)
+    d.v_cache = _dev(v_cache, "v_cache", torch.bfloat16)
+    d.num_blocks = N
+    d.q = _dev(q, "q", torch.bfloat16)
+    d.out = _dev(out, "out", torch.bfloat16)
+    d.block_tables = _dev(block_tables, "block_tables", torch.int32)
+    d.block_table_stride = block_tables.stride(0)
+    d.context_lens = _dev(context_lens, "context_lens", torch.int32)
+    d.workspace = _dev(workspace, "workspace", workspace.dtype)
+    d.workspace_bytes = workspace.numel() * workspace.element_size()
+    d.num_q_heads, d.num_kv_heads, d.head_dim, d.block_size = q.shape[1], Hkv, D, B
+    d.scale = float(scale)
+    d.max_context_len = int(max_context_len)
+    for t, nm in ((key, "key"), (value, "value"), (slot_mapping, "slot_mapping"), (q, "q"), (out, "out"),
+                  (block_tables, "block_tables"), (context_lens, "context_lens")):
+        if t.shape[0] < rows:
+            raise ValueError(f"{nm} has {t.shape[0]} rows, the largest bucket needs {rows}")
+    return d
+
+
 class DecodeGraphs:
     """Decode-step graphs (``pkv_decode_graphs_*``) over static device
     buffers: key/value [rows, H_kv, D], slot_mapping [rows], q/out
     [rows, H_q, D], block_tables [rows, stride], context_lens [rows] and a
     workspace sized for the largest bucket. The tensors are kept alive with
     the handle; fill rows [0, batch), pad the rest up to the bucket (slot -1,
-    context 0) and call ``launch(batch)``."""
+    context 0) and call ``launch(batch)``. ``layers`` (optional) lists further
+    layers as (key, value, k_cache, v_cache, q, out) tuples sharing the
+    metadata and the workspace; each replay then runs every layer in order
+    (``pkv_decode_graphs_create_layers``)."""
 
     def __init__(self, key, value, slot_mapping, k_cache, v_cache, q, out, block_tables, context_lens, workspace,
-                 scale, max_context_len, buckets):
-        torch = _torch()
+                 scale, max_context_len, buckets, layers=()):
         self._lib = load_library()
-        self._keep = (key, value, slot_mapping, k_cache, v_cache, q, out, block_tables, context_lens, workspace)
-        N, B, Hkv, D = k_cache.shape
-        d = DecodeGraphDesc()
-        d.key = _dev(key, "key", torch.bfloat16, False)
-        d.key_stride = key.stride(0)
-        d.value = _dev(value, "value", torch.bfloat16, False)
-        d.value_stride = value.stride(0)
-        d.slot_mapping = _dev(slot_mapping, "slot_mapping", torch.int32)
-        d.k_cache = _dev(k_cache, "k_cache", torch.bfloat16)
-        d.v_cache = _dev(v_cache, "v_cache", torch.bfloat16)
-        d.num_blocks = N
-        d.q = _dev(q, "q", torch.bfloat16)
-        d.out = _dev(out, "out", torch.bfloat16)
-        d.block_tables = _dev(block_tables, "block_tables", torch.int32)
-        d.block_table_stride = block_tables.stride(0)
-        d.context_lens = _dev(context_lens, "context_lens", torch.int32)
-        d.workspace = _dev(workspace, "workspace", workspace.dtype)
-        d.workspace_bytes = workspace.numel() * workspace.element_size()
-        d.num_q_heads, d.num_kv_heads, d.head_dim, d.block_size = q.shape[1], Hkv, D, B
-        d.scale = float(scale)
-        d.max_context_len = int(max_context_len)
-        rows = max(buckets)
-        for t, nm in ((key, "key"), (value, "value"), (slot_mapping, "slot_mapping"), (q, "q"), (out, "out"),
-                      (block_tables, "block_tables"), (context_lens, "context_lens")):
-            if t.shape[0] < rows:
-                raise ValueError(f"{nm} has {t.shape[0]} rows, the largest bucket needs {rows}")
         self.buckets = sorted(int(b) for b in buckets)
+        rows = max(self.buckets)
+        all_layers = [(key, value, k_cache, v_cache, q, out)] + list(layers)
+        self._keep = (all_layers, slot_mapping, block_tables, context_lens, workspace)
+        descs = (DecodeGraphDesc * len(all_layers))()
+        for i, (k, v, kc, vc, qq, oo) in enumerate(all_layers):
+            descs[i] = _graph_desc(k, v, slot_mapping, kc, vc, qq, oo, block_tables, context_lens, workspace, scale,
+                                   max_context_len, rows)
         arr = (ctypes.c_int32 * len(self.buckets))(*self.buckets)
         h = c_vp()
-        _check("pkv_decode_graphs_create", self._lib.pkv_decode_graphs_create(ctypes.byref(d), arr, len(self.buckets),
-                                                                              ctypes.byref(h)))
+        _check("pkv_decode_graphs_create",
+               self._lib.pkv_decode_graphs_create_layers(descs, len(all_layers), arr, len(self.buckets),
+                                                         ctypes.byref(h)))
         self._h = h
 
     def launch(self, batch: int, stream=None) -> int:

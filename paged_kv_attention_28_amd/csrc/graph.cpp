@@ -1,6 +1,7 @@
 // Decode-step graphs: one HIP graph per batch bucket, each holding the step's
 // KV store fused into paged decode attention (split pass + merge) on static
-// buffers: two kernels per step.
+// buffers, for one layer or for every layer of the model in order: two
+// kernels per layer.
 //
 // P1 = "13. 读一个最小推理引擎：nano-vllm", "第五站：执行准备与 KV 容量" (CUDA
 // Graph paragraph): decode only, one graph per bucket (1, 2, 4, 8, then
@@ -22,7 +23,7 @@
 #include "common.h"
 
 struct pkv_decode_graphs {
-  pkv_decode_graph_desc d{};
+  std::vector<pkv_decode_graph_desc> layers;  // one step = these descriptors' calls, in order
   std::vector<int32_t> buckets;       // ascending
   std::vector<hipGraphExec_t> execs;  // one per bucket
   std::vector<hipGraph_t> graphs;
@@ -36,32 +37,44 @@ struct pkv_decode_graphs {
 
 namespace {
 
-// the decode step on the first `rows` rows of the static buffers
-pkv_status enqueue_step(const pkv_decode_graph_desc& d, int32_t rows, hipStream_t s) {
-  return paged_attn_decode_store(d.out, d.q, d.key, d.key_stride, d.value, d.value_stride, d.slot_mapping, d.k_cache,
-                                 d.v_cache, d.block_tables, d.block_table_stride, d.context_lens, rows, d.num_q_heads,
-                                 d.num_kv_heads, d.head_dim, d.block_size, d.num_blocks, d.scale, d.max_context_len,
-                                 d.workspace, d.workspace_bytes, s);
+// the decode step (every layer's store + attention) on the first `rows` rows of the static buffers
+pkv_status enqueue_step(const std::vector<pkv_decode_graph_desc>& layers, int32_t rows, hipStream_t s) {
+  for (const pkv_decode_graph_desc& d : layers) {
+    const pkv_status st = paged_attn_decode_store(
+        d.out, d.q, d.key, d.key_stride, d.value, d.value_stride, d.slot_mapping, d.k_cache, d.v_cache,
+        d.block_tables, d.block_table_stride, d.context_lens, rows, d.num_q_heads, d.num_kv_heads, d.head_dim,
+        d.block_size, d.num_blocks, d.scale, d.max_context_len, d.workspace, d.workspace_bytes, s);
+    if (st != PKV_OK) return st;
+  }
+  return PKV_OK;
 }
 
 }  // namespace
 
 extern "C" pkv_status pkv_decode_graphs_create(const pkv_decode_graph_desc* desc, const int32_t* buckets,
                                                int32_t num_buckets, pkv_decode_graphs** out) {
+  return pkv_decode_graphs_create_layers(desc, 1, buckets, num_buckets, out);
+}
+
+extern "C" pkv_status pkv_decode_graphs_create_layers(const pkv_decode_graph_desc* layers, int32_t num_layers,
+                                                      const int32_t* buckets, int32_t num_buckets,
+                                                      pkv_decode_graphs** out) {
   using pkv::fail;
   if (!out) return fail(PKV_ERR_INVALID, "pkv_decode_graphs_create: null output");
   *out = nullptr;
-  if (!desc || !buckets || num_buckets < 1) return fail(PKV_ERR_INVALID, "pkv_decode_graphs_create: no buckets");
+  if (!layers || num_layers < 1) return fail(PKV_ERR_INVALID, "pkv_decode_graphs_create: no layers");
+  if (!buckets || num_buckets < 1) return fail(PKV_ERR_INVALID, "pkv_decode_graphs_create: no buckets");
   for (int32_t i = 0; i < num_buckets; ++i)
     if (buckets[i] < 1 || (i && buckets[i] <= buckets[i - 1]))
       return fail(PKV_ERR_INVALID, "pkv_decode_graphs_create: buckets must be positive and ascending");
   // argument errors surface from the entry points while the first graph is
   // captured; the decode launch's device queries are made here, outside capture
-  for (int32_t i = 0; i < num_buckets; ++i)
-    if (!pkv::decode_prepare(desc->num_q_heads, desc->num_kv_heads, buckets[i])) break;
+  for (int32_t l = 0; l < num_layers; ++l)
+    for (int32_t i = 0; i < num_buckets; ++i)
+      if (!pkv::decode_prepare(layers[l].num_q_heads, layers[l].num_kv_heads, buckets[i])) break;
   pkv_decode_graphs* g = new (std::nothrow) pkv_decode_graphs;
   if (!g) return fail(PKV_ERR_INVALID, "pkv_decode_graphs_create: out of host memory");
-  g->d = *desc;
+  g->layers.assign(layers, layers + num_layers);
   g->buckets.assign(buckets, buckets + num_buckets);
   g->execs.assign(num_buckets, nullptr);
   g->graphs.assign(num_buckets, nullptr);
@@ -77,7 +90,7 @@ extern "C" pkv_status pkv_decode_graphs_create(const pkv_decode_graph_desc* desc
       result = fail(PKV_ERR_HIP, "pkv_decode_graphs_create: begin capture: %s", hipGetErrorString(e));
       break;
     }
-    pkv_status st = enqueue_step(g->d, g->buckets[i], cs);
+    pkv_status st = enqueue_step(g->layers, g->buckets[i], cs);
     hipGraph_t graph = nullptr;
     e = hipStreamEndCapture(cs, &graph);
     g->graphs[i] = graph;

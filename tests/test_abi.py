@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(P.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.pkv_abi_version() == 9
+    assert lib.pkv_abi_version() == 10
 
 
 def test_product_package_does_not_import_oracle():

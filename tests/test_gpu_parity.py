@@ -629,6 +629,82 @@ def test_decode_graphs_replay_matches_eager():
     graphs.close()
 
 
+def test_decode_step_graphs_all_layers_match_eager():
+    """Graphs holding a whole decode step of several layers (each layer's fused store + decode, one replay per
+    step) give every layer's eager bits on the same buffers, for exact and padded buckets, three replays each
+    with unrelated eager work in between; layer outputs and caches also match the oracle."""
+    import paged_kv_attention_28_amd as P
+    rng = np.random.default_rng(33)
+    lens = [int(x) for x in rng.integers(1, 1200, size=48)]
+    nl, rows, buckets = 4, 48, [1, 2, 4, 8, 16, 32, 48]
+    ws_layers = []
+    for l in range(nl):            # the same lengths and block tables in every layer, each with its own values
+        w = custom(lens, [L - 1 for L in lens], kind="decode", seed=40)
+        w.seed = 1000 + l
+        ws_layers.append(w)
+    dws = [H.DeviceWorkload(w).build() for w in ws_layers]     # each layer: its own caches, after the step's store
+    w0 = ws_layers[0]
+    q_all = [dw.pass_inputs(w.passes[0])[0] for dw, w in zip(dws, ws_layers)]
+    m_all = dws[0].pass_inputs(w0.passes[0])[1]                # tables and lengths: the same for every layer
+    kv_all = [W.store_kv(w, "cuda") for w in ws_layers]
+    slot_all = dws[0].store_slots()
+    mb, max_ctx = w0.max_blocks_per_seq, w0.max_blocks_per_seq * 256
+    dev = "cuda"
+    slots = torch.full((rows,), -1, dtype=torch.int32, device=dev)
+    bt = torch.full((rows, mb), -1, dtype=torch.int32, device=dev)
+    ctx = torch.zeros(rows, dtype=torch.int32, device=dev)
+    bufs = [dict(key=torch.zeros(rows, 8, 128, dtype=torch.bfloat16, device=dev),
+                 value=torch.zeros(rows, 8, 128, dtype=torch.bfloat16, device=dev),
+                 q=torch.zeros(rows, 16, 128, dtype=torch.bfloat16, device=dev),
+                 out=torch.empty(rows, 16, 128, dtype=torch.bfloat16, device=dev)) for _ in range(nl)]
+    ws = torch.empty(P.paged_attn_decode_workspace_size(rows, 16, 8, 128, max_ctx), dtype=torch.uint8, device=dev)
+    b0 = bufs[0]
+    graphs = P.DecodeGraphs(b0["key"], b0["value"], slots, dws[0].k_cache, dws[0].v_cache, b0["q"], b0["out"], bt,
+                            ctx, ws, w0.scale, max_ctx, buckets,
+                            layers=[(b["key"], b["value"], dw.k_cache, dw.v_cache, b["q"], b["out"])
+                                    for b, dw in zip(bufs[1:], dws[1:])])
+    junk = torch.randn(512, 512, device=dev)
+    kc_eager = [(dw.k_cache.clone(), dw.v_cache.clone()) for dw in dws]
+    for batch in (1, 3, 17, 48):
+        bucket = min(b for b in buckets if b >= batch)
+        print(f"[step graphs] {nl} layers, batch {batch} (bucket {bucket})", flush=True)
+        slots.fill_(-1), bt.fill_(-1), ctx.zero_()
+        slots[:batch], bt[:batch], ctx[:batch] = slot_all[:batch], m_all.block_tables[:batch], m_all.context_lens[:batch]
+        for l, b in enumerate(bufs):
+            for t in b.values():
+                t.zero_()
+            b["key"][:batch], b["value"][:batch] = kv_all[l][0][:batch], kv_all[l][1][:batch]
+            b["q"][:batch] = q_all[l][:batch]
+        # eager reference: the same calls on copies of the caches
+        refs = []
+        for l, b in enumerate(bufs):
+            kc, vc = kc_eager[l]
+            o = torch.empty(bucket, 16, 128, dtype=torch.bfloat16, device=dev)
+            P.binding.paged_attn_decode_store(o, b["q"][:bucket], b["key"][:bucket], b["value"][:bucket],
+                                              slots[:bucket], kc, vc, bt[:bucket], ctx[:bucket], w0.scale, max_ctx, ws)
+            refs.append(o)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for b in bufs:
+                b["out"].fill_(7.0)
+            assert graphs.launch(batch) == bucket
+            torch.cuda.synchronize()
+            for l, b in enumerate(bufs):
+                assert torch.equal(b["out"][:bucket].view(torch.int16), refs[l].view(torch.int16)), (batch, rep, l)
+                assert (b["out"][batch:bucket].float() == 0).all()
+            (junk @ junk).sum().item()
+        for l, dw in enumerate(dws):
+            assert torch.equal(dw.k_cache.view(torch.int16), kc_eager[l][0].view(torch.int16))
+            assert torch.equal(dw.v_cache.view(torch.int16), kc_eager[l][1].view(torch.int16))
+    for l in (0, nl - 1):
+        w = ws_layers[l]
+        kc_ref, vc_ref = O.build_caches(w, device="cuda")
+        assert np.array_equal(_cache_bits(dws[l].k_cache), kc_ref)
+        oracle = O.run_pass(w, w.passes[0], kc_ref, vc_ref, q=q_all[l])
+        assert_close(bufs[l]["out"][:48], oracle[:48], None, f"step graph layer {l}")
+    graphs.close()
+
+
 def _within_one_bf16_unit(gpu, ref, what):
     """|gpu - ref| within one bf16 unit of the exact value (1e-5 floor for
     results near zero, where the fp32 products' own rounding dominates)."""
