@@ -246,15 +246,15 @@ class TraceRunner:
         v = W.randn_bf16(self.seed, s, W.TAG_V, (rows, self.hkv, self.d), self.device)
         return q, k, v
 
-    def run(self, steps, keep=None, timing=None, fused_decode=False):
+    def run(self, steps, keep=None, timing=None, fused=False):
         """steps: ``binding.SchedStep`` list (step i has index i). keep:
         {step index: layers} whose attention outputs are returned (on the
         host) as {(step index, layer): tensor}. timing: a list that receives
         (step index, layer, e0, e1, e2): HIP events recorded on the current
         stream before the layer's store, between store and attention, and
-        after attention (the q/k/v draws stay outside). fused_decode: decode
-        steps store inside the attention call (paged_attn_decode_store; e0
-        and e1 then mark the same point)."""
+        after attention (the q/k/v draws stay outside). fused: every
+        step stores inside its attention call (paged_attn_decode_store,
+        paged_attn_prefill_store; e0 and e1 then mark the same point)."""
         kept = {}
         for i, st in enumerate(steps):
             m = B.pkv_prepare_step(st.seq_lens, st.num_cached, st.block_tables, W.BLOCK_SIZE, self.mb, st.num_pad)
@@ -262,7 +262,6 @@ class TraceRunner:
             for layer in range(self.L):
                 q, k, v = self.values(i, layer, m.num_tokens)
                 kc, vc = self.caches[layer]
-                fused = fused_decode and st.kind == "decode"
                 if timing is not None:
                     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
                     ev[0].record()
@@ -271,9 +270,13 @@ class TraceRunner:
                 if timing is not None:
                     ev[1].record()
                 out = torch.empty_like(q)
-                if fused:
+                if fused and st.kind == "decode":
                     B.paged_attn_decode_store(out, q, k, v, dm.slot_mapping, kc, vc, dm.block_tables, dm.context_lens,
                                               self.scale, dm.max_context_len, self.workspace)
+                elif fused:
+                    B.paged_attn_prefill_store(out, q, k, v, dm.slot_mapping, kc, vc, dm.cu_seqlens_q, dm.context_lens,
+                                               dm.block_tables, dm.max_q_len, dm.max_context_len, self.scale,
+                                               work_items=dm.work_items)
                 elif st.kind == "decode":
                     B.paged_attn_decode(out, q, kc, vc, dm.block_tables, dm.context_lens, self.scale,
                                         dm.max_context_len, self.workspace)

@@ -804,15 +804,16 @@ def test_sampler_matches_oracle_decision(rows, vocab, pad):
 # configuration 5: scheduler-trace replay over 28 layers
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("fused_decode", [False, True])
-def test_scheduler_trace_replay(fused_decode):
+@pytest.mark.parametrize("fused", [False, True])
+def test_scheduler_trace_replay(fused):
     """The native scheduler's steps (identical to the oracle scheduler's,
     checked first) replayed on the GPU for all 28 layers; layers 0 and 27
     mirrored on the host and compared at sampled steps: the first prefill,
     the re-prefill after the first preemption, and decode steps including
-    the one that preempted, a middle one and the last. With fused_decode the
-    decode steps store inside the attention call (paged_attn_decode_store),
-    so later steps also read the rows it wrote."""
+    the one that preempted, a middle one and the last. With fused every step
+    stores inside its attention call (paged_attn_decode_store,
+    paged_attn_prefill_store), so later steps also read the rows those calls
+    wrote."""
     import paged_kv_attention_28_amd as P
     from oracle import sched as OS
     from workloads import sched as S
@@ -830,7 +831,7 @@ def test_scheduler_trace_replay(fused_decode):
     sample = sorted({0, reprefill, dec[0], pre_idx, dec[len(dec) // 2], dec[-1]})
     layers = (0, S.NUM_LAYERS - 1)
     runner = H.TraceRunner(W.SEEDS[5], S.NUM_LAYERS, S.POOL_BLOCKS)
-    kept = runner.run(native, keep={i: layers for i in sample}, fused_decode=fused_decode)
+    kept = runner.run(native, keep={i: layers for i in sample}, fused=fused)
     torch.cuda.synchronize()
     n = O.trace_check(runner, steps, kept, layers)
     assert n == len(sample) * len(layers)
