@@ -25,6 +25,32 @@ pkv_status ok();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The step's new K/V rows for the fused store forms (paged_attn_decode_store,
+// paged_attn_prefill_store): a token's row is read from k / v (the step's
+// input, `*_stride_b` bytes apart) instead of the cache and written to its
+// cache row slots[token]. k == nullptr when the caller stored the rows
+// beforehand (paged_attn_decode, paged_attn_prefill_varlen).
+struct NewRows {
+  const char* k;
+  const char* v;
+  int64_t k_stride_b, v_stride_b;  // bytes between tokens' (decode: sequences') rows
+  const int32_t* slots;            // one slot per token (decode: per sequence)
+  int64_t num_slots;               // rows in each cache
+  char* k_cache;                   // the caches, writable (only the slots' rows are written)
+  char* v_cache;
+};
+
+// Decode on the MFMA tile kernel of the prefill path (its query is the
+// sequence's one new token, at position context_lens[s] - 1): one
+// work-group per (KV head, sequence), no workspace, no merge. Used by
+// paged_attn_decode* for eight query heads per KV head, where the row-wide
+// decode kernel is bound by its vector arithmetic. Arguments as validated by
+// the decode entry points; head_dim 128, block 256.
+pkv_status decode_tile_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int64_t num_blocks,
+                            float scale, int32_t max_context_len, void* stream, const NewRows& nr);
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -60,6 +60,8 @@ constexpr int kWavesCap = 4096;    // persistent grid cap (partial slots are siz
 constexpr int kMinStepsPerWave = 4;
 constexpr int kWideMergeMaxSeqs = 32;  // batches up to this size merge per (sequence, head)
 constexpr int kMaxSeqs = 8192;     // LDS scan capacity
+// eight query heads per KV head: from this many (sequence, KV head) pairs on, decode runs on the MFMA tile form
+constexpr int64_t kTileDecodeMinPairs = 512;
 // LDS reserved per stream work-group: more than half a CU's 160 KiB, so each
 // CU holds one work-group (one wavefront per SIMD). On the 256-sequence
 // decode workload this ran 6.5 % faster than two per CU: each wavefront walks
@@ -121,19 +123,10 @@ struct Step {
   int32_t slot;            // fused store: cache row of the new token on the sequence's last step, else -1
 };
 
-// The step's new K/V rows for the fused store (paged_attn_decode_store): row b
-// of k / v is sequence b's token at position context_lens[b] - 1, read from
-// there instead of the cache and written to cache row slots[b]. k == nullptr
-// when the caller stored the rows beforehand (paged_attn_decode).
-struct NewRows {
-  const char* k;
-  const char* v;
-  int64_t k_stride_b, v_stride_b;  // bytes between sequences' rows
-  const int32_t* slots;
-  int64_t num_slots;
-  char* k_cache;  // the caches, writable (only the slots' rows are written)
-  char* v_cache;
-};
+// The step's new K/V rows (NewRows, common.h) for the fused store
+// (paged_attn_decode_store): row b of k / v is sequence b's token at position
+// context_lens[b] - 1, read from there instead of the cache and written to
+// cache row slots[b].
 
 template <int HKV>
 __device__ __forceinline__ void load_buf(Buf& x, const char* __restrict__ kc, const char* __restrict__ vc,
@@ -872,6 +865,16 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
     if (reinterpret_cast<uintptr_t>(workspace) & 255)
       return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: workspace must be 256-byte aligned");
   }
+
+  // Eight query heads per KV head: the row-wide kernel below is bound by its vector arithmetic there
+  // (4.0-4.3 TB/s), so calls with enough (sequence, KV head) pairs for the tile form's one work-group per
+  // pair go to it instead (no workspace, no merge). Measured on MI355X, 64 Q / 8 KV: contexts of 100-2048
+  // tokens from 16 sequences up (37.5 vs 45.2 us at 16, 222 vs 282 us at 256), 4096-32768 tokens from 64
+  // sequences up (972 vs 1061 us; at 32 sequences 781 vs 555 us, a few long pairs set the time).
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  if (G == 8 && (pairs >= kTileDecodeMinPairs || (pairs >= kTileDecodeMinPairs / 4 && max_context_len <= 4096)))
+    return decode_tile_call(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs,
+                            num_q_heads, num_kv_heads, num_blocks, scale, max_context_len, stream, nr);
 
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = stream_lds(num_seqs);

@@ -162,20 +162,11 @@ __device__ __forceinline__ void issue_tile(char* kbuf, char* vbuf, const char* _
 #pragma clang diagnostic pop
 }
 
-// The step's new K/V rows for the fused store (paged_attn_prefill_store):
-// positions >= num_cached of a sequence are read from the step's key/value
-// input (token q0 + p - c of the step) instead of the cache, and each
-// work-group writes its own query tokens' rows of its KV head to their
-// slots. k == nullptr when the caller stored the rows beforehand.
-struct NewRows {
-  const char* k;
-  const char* v;
-  int64_t k_stride_b, v_stride_b;  // bytes between tokens
-  const int32_t* slots;            // the step's slot mapping, one slot per token
-  int64_t num_slots;               // rows in each cache
-  char* k_cache;                   // the caches, writable (only the slots' rows are written)
-  char* v_cache;
-};
+// The step's new K/V rows (NewRows, common.h) for the fused store
+// (paged_attn_prefill_store): positions >= num_cached of a sequence are read
+// from the step's key/value input (token q0 + p - c of the step) instead of
+// the cache, and each work-group writes its own query tokens' rows of its KV
+// head to their slots.
 
 // issue_tile for a tile that holds new tokens: rows r < cut (positions < c)
 // from the cache (descriptor as in issue_tile), rows r >= cut from the
@@ -230,7 +221,12 @@ __device__ __forceinline__ void issue_tile_new(char* kbuf, char* vbuf, const cha
 #pragma clang diagnostic pop
 }
 
-template <int G, bool FUSED>
+// DECODE: the decode form (decode_tile_call). The grid is (KV head,
+// sequence); the query is the sequence's one new token (row s of q and out,
+// position context_lens[s] - 1), so only the first wavefront holds query
+// rows (the others still move their share of every tile); an empty context
+// gives zero output rows.
+template <int G, bool FUSED, bool DECODE = false>
 __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kernel(
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
     const int32_t* __restrict__ context_lens, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
@@ -246,7 +242,11 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
   // work item: from the host plan (one per non-empty tile, heaviest first),
   // else from the grid (kv_head, seq, q-tile counted from the end)
   int g, b, tile;
-  if (items) {
+  if (DECODE) {
+    g = blockIdx.x;
+    b = blockIdx.y;
+    tile = 0;
+  } else if (items) {
     const int2 it = items[blockIdx.x];
     b = it.x;
     g = it.y & 255;
@@ -257,11 +257,19 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
     b = blockIdx.y;
     tile = -1 - (int)blockIdx.z;  // resolved once the tile count is known
   }
-  const int q0 = cu_seqlens_q[b];
-  int n = cu_seqlens_q[b + 1] - q0;
+  const int q0 = DECODE ? b : cu_seqlens_q[b];
+  int n = DECODE ? 1 : cu_seqlens_q[b + 1] - q0;
   n = n > max_q ? max_q : n;
   int L = context_lens[b];
   L = L > max_ctx ? max_ctx : L;
+  if (DECODE && L <= 0) {  // empty context: zero output for this KV head's query heads
+    if ((int)threadIdx.x < 16 * G) {
+      const int h = (int)threadIdx.x >> 4;
+      *reinterpret_cast<u32x4*>(out + ((int64_t)b * hq + g * G + h) * kHeadDim + 8 * (threadIdx.x & 15)) =
+          u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
   const int c = L - n;
   if (n <= 0 || c < 0) return;
   const int ntiles = (n + kTokWG - 1) / kTokWG;
@@ -641,6 +649,36 @@ pkv_status prefill_call(void* out, const void* q, const int32_t* cu_seqlens_q, c
 }
 
 }  // namespace
+}  // namespace pkv
+
+namespace pkv {
+
+pkv_status decode_tile_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int64_t num_blocks,
+                            float scale, int32_t max_context_len, void* stream, const NewRows& nr) {
+  if (num_q_heads != 8 * num_kv_heads)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: the tile form takes 8 query heads per KV head");
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: more than 65535 sequences");
+  if (num_seqs == 0) return ok();
+  const float scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid(num_kv_heads, num_seqs);
+  uint16_t* o = static_cast<uint16_t*>(out);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const char* kc = static_cast<const char*>(k_cache);
+  const char* vc = static_cast<const char*>(v_cache);
+  if (nr.k)
+    hipLaunchKernelGGL((prefill_kernel<8, true, true>), grid, dim3(256), 0, s, o, qq, nullptr, context_lens, kc, vc,
+                       block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2, 1,
+                       max_context_len, nullptr, num_seqs, nr);
+  else
+    hipLaunchKernelGGL((prefill_kernel<8, false, true>), grid, dim3(256), 0, s, o, qq, nullptr, context_lens, kc,
+                       vc, block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2, 1,
+                       max_context_len, nullptr, num_seqs, nr);
+  return check_launch("paged_attn_decode (tile form)");
+}
+
 }  // namespace pkv
 
 extern "C" pkv_status paged_attn_prefill_varlen(void* out, const void* q, const int32_t* cu_seqlens_q,

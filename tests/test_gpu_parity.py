@@ -254,6 +254,16 @@ EDGE = {
     "decode_hkv4_gqa4_long": _dec([5000, 4097, 100], hq=16, hkv=4, **PEAKY),
     "prefill_hkv4_gqa2": dict(lens=[300, 129, 1000], cached=[0, 100, 511], hq=8, hkv=4),
     "prefill_hkv4_gqa4": dict(lens=[257, 700], cached=[0, 256], hq=16, hkv=4),
+    # eight query heads per KV head on enough (sequence, KV head) pairs: the MFMA tile form of decode
+    # (contexts up to 4096 from 16 sequences, longer from 64), with its empty-context rows, one-token
+    # contexts, peaky and rising scores
+    "decode_tile_gqa8": _dec([(61 * i) % 2100 + 1 for i in range(24)], hq=64),
+    "decode_tile_gqa8_pad": dict(lens=[1, 1, 2, 700] + [(37 * i) % 500 + 3 for i in range(14)],
+                                 cached=[0, 0, 1, 699] + [(37 * i) % 500 + 2 for i in range(14)], hq=64,
+                                 kind="decode", pad=3),
+    "decode_tile_gqa8_long": _dec([(97 * i) % 600 + 1 for i in range(60)] + [4200, 5000, 4097, 6100], hq=64),
+    "decode_tile_gqa8_peaky": _dec([(53 * i) % 1800 + 1 for i in range(20)], hq=64, **PEAKY),
+    "decode_tile_gqa8_ramp": _dec([(71 * i) % 3000 + 1 for i in range(20)], hq=64, **RAMP),
     # more than 32 sequences with 8 and 4 query heads: the per-sequence (serial) merge
     "decode_hq8_hkv4_40seqs": _dec([(41 * i) % 900 + 1 for i in range(40)], hq=8, hkv=4),
     "decode_hq4_hkv1_40seqs": _dec([(29 * i) % 1300 + 1 for i in range(40)], hq=4, hkv=1),
@@ -283,11 +293,19 @@ def test_edge_parity(name):
                 assert torch.equal(out[b, h].view(torch.int16), nv[b, h // G].view(torch.int16))
     if name == "decode_pad_rows":
         assert (_f64(out[2:]) == 0).all()
+    if name == "decode_tile_gqa8_pad":
+        G = w.num_q_heads // w.num_kv_heads
+        nk, nv = W.store_kv(w, "cuda")
+        for b in (0, 1):  # one-token contexts return their V row exactly
+            for h in range(w.num_q_heads):
+                assert torch.equal(out[b, h].view(torch.int16), nv[b, h // G].view(torch.int16))
+        assert (_f64(out[18:]) == 0).all()  # padding rows (empty contexts) are zero
 
 
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
                "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
-               "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs"]
+               "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs", "decode_tile_gqa8_pad",
+               "decode_tile_gqa8_long"]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES)
@@ -569,16 +587,18 @@ def test_binding_launches_on_current_stream():
     assert torch.equal(kflat[rows].view(torch.int16), key.view(torch.int16))
 
 
-def test_decode_graphs_replay_matches_eager():
+@pytest.mark.parametrize("hq", [16, 64])
+def test_decode_graphs_replay_matches_eager(hq):
     """Decode-step graphs (the fused store + decode per bucket) give the bits
     of the eager kv_store and paged_attn_decode calls on the same static buffers, for batches that hit an exact
     bucket and batches that need padding rows; each graph is replayed three
     times with unrelated eager work and synchronisation in between, and the
-    real rows are also checked against the oracle."""
+    real rows are also checked against the oracle. With 64 query heads (8 per KV head) the buckets of 16
+    rows and up run the MFMA tile form of decode, the smaller ones the row-wide kernel."""
     import paged_kv_attention_28_amd as P
     rng = np.random.default_rng(31)
     lens = [int(x) for x in rng.integers(1, 1500, size=64)]
-    w = custom(lens, [L - 1 for L in lens], kind="decode", seed=31)
+    w = custom(lens, [L - 1 for L in lens], kind="decode", seed=31, hq=hq)
     dw = H.DeviceWorkload(w).build()
     kc_ref, vc_ref = O.build_caches(w, device="cuda")
     p = w.passes[0]
@@ -590,12 +610,12 @@ def test_decode_graphs_replay_matches_eager():
     key = torch.zeros(rows, 8, 128, dtype=torch.bfloat16, device=dev)
     value = torch.zeros_like(key)
     slots = torch.full((rows,), -1, dtype=torch.int32, device=dev)
-    q = torch.zeros(rows, 16, 128, dtype=torch.bfloat16, device=dev)
+    q = torch.zeros(rows, hq, 128, dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(q)
     bt = torch.full((rows, mb), -1, dtype=torch.int32, device=dev)
     ctx = torch.zeros(rows, dtype=torch.int32, device=dev)
     max_ctx = mb * 256
-    ws = torch.empty(P.paged_attn_decode_workspace_size(rows, 16, 8, 128, max_ctx), dtype=torch.uint8, device=dev)
+    ws = torch.empty(P.paged_attn_decode_workspace_size(rows, hq, 8, 128, max_ctx), dtype=torch.uint8, device=dev)
     graphs = P.DecodeGraphs(key, value, slots, dw.k_cache, dw.v_cache, q, out, bt, ctx, ws, w.scale, max_ctx, buckets)
     ws_eager = torch.empty_like(ws)
     junk = torch.randn(512, 512, device=dev)
@@ -610,7 +630,7 @@ def test_decode_graphs_replay_matches_eager():
         torch.cuda.synchronize()
         # eager reference on the same buffers and the same bucket of rows
         P.kv_store(key[:bucket], value[:bucket], dw.k_cache, dw.v_cache, slots[:bucket])
-        ref = torch.empty(bucket, 16, 128, dtype=torch.bfloat16, device=dev)
+        ref = torch.empty(bucket, hq, 128, dtype=torch.bfloat16, device=dev)
         P.paged_attn_decode(ref, q[:bucket], dw.k_cache, dw.v_cache, bt[:bucket], ctx[:bucket], w.scale, max_ctx,
                             ws_eager)
         torch.cuda.synchronize()
