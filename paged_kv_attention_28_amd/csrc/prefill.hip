@@ -57,6 +57,10 @@
 //  * K operands are read four ahead of the S^T products (schedule pinned with
 //    sched_group_barrier), and the P V^T products run key-chunk outer, so the
 //    second half of the exponentials overlaps the first four products.
+//  * A decode form (decode_tile_call) runs the same kernel with each
+//    sequence's one new token as the query, one work-group per (KV head,
+//    sequence): decode with eight query heads per KV head, whose arithmetic
+//    per byte is too heavy for the row-wide decode kernel's vector FMAs.
 //  * The output leaves through LDS: the accumulators hold O^T (a lane owns one
 //    query row, 8-byte runs of dims), so each wavefront stages its 32 rows in
 //    LDS and writes whole 256-byte rows, 16 bytes per lane; stored directly,
@@ -239,8 +243,9 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
                                                                                        : 4 * 32 * kRowBytes];
   __shared__ int32_t own_slots[FUSED ? kTokWG : 1];  // fused store: the slots of this work-group's query tokens
 
-  // work item: from the host plan (one per non-empty tile, heaviest first),
-  // else from the grid (kv_head, seq, q-tile counted from the end)
+  // work item: the decode form's (kv_head, seq) grid; else from the host plan
+  // (one per non-empty tile, heaviest first), else from the grid (kv_head,
+  // seq, q-tile counted from the end)
   int g, b, tile;
   if (DECODE) {
     g = blockIdx.x;
