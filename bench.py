@@ -23,7 +23,9 @@ the distinct context K/V rows), and the same call launched back to back for
 0.1 s (the shader clock under this load depends on how busy the GPU is kept).
 ``long_decode`` times the decode step of the long-context workload (512
 sequences, contexts U[4096, 32768], 32 Q / 8 KV heads, about 38.7 GB of K/V
-per call) against the HBM peak. ``hbm_copy_ceiling`` is torch's own copy over
+per call) against the HBM peak. ``decode_gqa8`` times decode with eight query
+heads per KV head (64 Q / 8 KV, 256 sequences of 100-2048 tokens), the shape
+that runs on the MFMA tile form. ``hbm_copy_ceiling`` is torch's own copy over
 2 GiB. ``trace_replay`` replays
 the 28-layer scheduler trace (256 requests) and reports decode GB/s, prefill
 TFLOP/s and kernel-only tokens/s from events around each layer's kernels. ``cpu_baseline`` times the
@@ -602,6 +604,53 @@ def long_decode(torch, dev, steps: int, warmup: int) -> dict:
     return out
 
 
+def decode_gqa8(torch, dev, reps: int = 30) -> dict:
+    """Decode with eight query heads per KV head (64 Q / 8 KV), 256 sequences of U[100, 2048] tokens on a
+    shuffled pool: paged_attn_decode back to back (HIP events around `reps` calls on the stream). This shape
+    runs on the MFMA tile form (one work-group per sequence and KV head)."""
+    from paged_kv_attention_28_amd import binding as B
+    rng = np.random.default_rng(8)
+    S, hq, hkv, d = 256, 64, 8, 128
+    lens = rng.integers(100, 2049, size=S).astype(np.int32)
+    nbs = (lens + 255) // 256
+    perm = rng.permutation(int(nbs.sum())).astype(np.int32)
+    bt_h = np.zeros((S, int(nbs.max())), dtype=np.int32)
+    off = 0
+    for i in range(S):
+        bt_h[i, :nbs[i]] = perm[off:off + nbs[i]]
+        off += nbs[i]
+    g = torch.Generator(device=dev).manual_seed(8)
+    kc = torch.randn((int(nbs.sum()), 256, hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn_like(kc)
+    q = torch.randn((S, hq, d), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(bt_h).to(dev)
+    ctx = torch.from_numpy(lens).to(dev)
+    max_ctx = int(lens.max())
+    ws = torch.empty(B.paged_attn_decode_workspace_size(S, hq, hkv, d, max_ctx), dtype=torch.uint8, device=dev)
+    scale = 1.0 / np.sqrt(d)
+    call = lambda: B.paged_attn_decode(out, q, kc, vc, bt, ctx, scale, max_ctx, ws)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    byts = int(lens.sum()) * hkv * 2 * d * 2 + 2 * S * hq * d * 2
+    gbs = byts / (us * 1e-6) / 1e9
+    log(f"[bench] decode 64 Q / 8 KV, 256 sequences: {us:.1f} us -> {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%} of HBM peak)")
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"workload": "decode, 256 seqs, context U[100, 2048], GQA 64Q/8KV (eight query heads per KV head), "
+                        "head_dim 128, bf16, block 256, shuffled pool; paged_attn_decode back to back",
+            "us": round(us, 2), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes": byts, "form": "MFMA tile form (one work-group per sequence and KV head)"}
+
+
 def graph_vs_eager(torch, dev, iters: int = 50, num_layers: int = 28):
     """A model's whole decode step, every layer's store + attention (28 layers of 16 Q / 8 KV x 128, each with
     its own caches), issued eagerly through the binding (one paged_attn_decode_store call per layer) versus
@@ -854,6 +903,7 @@ def main():
                    "rope_kv_store": rope}
 
     long_dec = None if args.no_long else long_decode(torch, dev, max(args.steps // 5, 5), 3)
+    gqa8 = decode_gqa8(torch, dev)
     graph = None if args.no_graph else graph_vs_eager(torch, dev)
     sampler = sampler_rate(torch, dev)
     trace = None if args.no_trace else trace_replay(torch)
@@ -892,6 +942,7 @@ def main():
         "decode_step_two_calls": two,
         "prefill": prefill,
         "long_decode": long_dec,
+        "decode_gqa8": gqa8,
         "decode_graph": graph,
         "sampler": sampler,
         "trace_replay": trace,
