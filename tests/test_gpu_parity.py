@@ -302,6 +302,49 @@ def test_edge_parity(name):
         assert (_f64(out[18:]) == 0).all()  # padding rows (empty contexts) are zero
 
 
+def _random_case(seed: int) -> dict:
+    """A seeded random shape: head counts from every supported G and KV-head count, batch size, lengths,
+    cached prefixes, padding rows and query scale drawn from `seed` (decode for even seeds, prefill for odd)."""
+    rng = np.random.default_rng(1000 + seed)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    q_mult = float(rng.choice([1.0, 1.0, 4.0]))
+    if seed >= 12:  # eight query heads per KV head on batches that reach the MFMA tile form of decode
+        hkv = 8
+        hq = 64
+        S = int(rng.integers(16, 65))
+        lens = [int(x) for x in rng.integers(1, 4097, size=S)]
+        return dict(lens=lens, cached=[L - 1 for L in lens], hq=hq, hkv=hkv, kind="decode",
+                    pad=int(rng.integers(0, 3)), q_mult=q_mult, seed=seed)
+    if seed % 2 == 0:
+        S = int(rng.integers(1, 41))
+        lens = [int(x) for x in rng.integers(1, 3001, size=S)]
+        return dict(lens=lens, cached=[L - 1 for L in lens], hq=hq, hkv=hkv, kind="decode",
+                    pad=int(rng.integers(0, 3)), q_mult=q_mult, seed=seed)
+    S = int(rng.integers(1, 9))
+    lens = [int(x) for x in rng.integers(1, 601, size=S)]
+    cached = [int(rng.integers(0, L)) if rng.random() < 0.6 else 0 for L in lens]
+    return dict(lens=lens, cached=cached, hq=hq, hkv=hkv, kind="prefill", q_mult=q_mult, seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shapes_parity(seed):
+    """Seeded random shapes (every G and KV-head count, ragged batches, cached prefixes, padding rows, wider
+    scores) against the oracle; decode calls that fit the MFMA tile form's rule take it."""
+    case = _random_case(seed)
+    print(f"[random] seed {seed}: {case['kind']} {len(case['lens'])} seqs, {case['hq']}Q/{case['hkv']}KV, "
+          f"max len {max(case['lens'])}, q x {case['q_mult']}", flush=True)
+    w = custom(**case)
+    dw = H.DeviceWorkload(w).build()
+    kc, vc = O.build_caches(w, device="cuda")
+    assert np.array_equal(_cache_bits(dw.k_cache), kc)
+    p = w.passes[0]
+    q, m = dw.pass_inputs(p)
+    out = dw.run_pass(p, q, m)
+    ref = O.run_pass(w, p, kc, vc, q=q)
+    assert_close(out, ref, m.host.cu_seqlens_q, f"random seed {seed}")
+
+
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
                "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
                "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs", "decode_tile_gqa8_pad",
