@@ -173,11 +173,14 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * wavefront), and partial results are combined in a fixed order that
  * depends on num_seqs (up to 32 sequences: 64 interleaved classes of pieces
  * per sequence and head, combined in a fixed tree; no atomics).
- * Eight query heads per KV head with num_seqs x num_kv_heads >= 512, or >= 128
- * with max_context_len <= 4096, run instead on the MFMA tile kernel of
- * paged_attn_prefill_varlen (the sequence's new token as its one query: one
- * work-group per (KV head, sequence), weights rounded to bf16 for the P.V
- * products); that form leaves the workspace untouched (it is still checked).
+ * Eight query heads per KV head run instead on the MFMA tile kernel of
+ * paged_attn_prefill_varlen (the sequence's new token as its one query,
+ * weights rounded to bf16 for the P.V products): one work-group per (KV head,
+ * sequence), or, when num_seqs x num_kv_heads < 1536, per (KV head,
+ * sequence, key chunk) with up to 16 chunks of at least 4 x 32 keys, whose
+ * partials (at most about 6.5 MB) go to the workspace and are merged by a
+ * second kernel in chunk order; the chunking depends only on num_seqs,
+ * num_kv_heads and max_context_len.
  */
 pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, int32_t block_table_stride,
@@ -203,11 +206,11 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
  *
  * Arguments: as for paged_attn_decode, without workspace / workspace_bytes.
  * Errors: as for paged_attn_decode, plus PKV_ERR_UNSUPPORTED when the
- * launch needs more than the 40 MiB (num_q_heads x 1040 bytes x 2 slots
- * per resident wavefront, plus 4 bytes per sequence: 32 query heads fit on
- * 1024 resident wavefronts, 64 do not, unless the call takes the tile form
- * described under paged_attn_decode, which uses no scratch) and PKV_ERR_HIP
- * when the array's device address cannot be found.
+ * launch needs more than the 40 MiB (num_q_heads x 1040 bytes, both partial
+ * slots, per resident wavefront, plus 4 bytes per sequence: 32 query heads
+ * fit on 1024 resident wavefronts; eight query heads per KV head take the tile form
+ * described under paged_attn_decode, whose partials need at most about
+ * 6.5 MB) and PKV_ERR_HIP when the array's device address cannot be found.
  */
 pkv_status paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, int32_t block_table_stride,

@@ -42,14 +42,17 @@ struct NewRows {
 
 // Decode on the MFMA tile kernel of the prefill path (its query is the
 // sequence's one new token, at position context_lens[s] - 1): one
-// work-group per (KV head, sequence), no workspace, no merge. Used by
+// work-group per (KV head, sequence), or per (KV head, sequence, key chunk)
+// with a merge when the pairs are too few to fill the GPU (partials in
+// `workspace`, which must hold them; else no split). Used by
 // paged_attn_decode* for eight query heads per KV head, where the row-wide
 // decode kernel is bound by its vector arithmetic. Arguments as validated by
 // the decode entry points; head_dim 128, block 256.
 pkv_status decode_tile_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int64_t num_blocks,
-                            float scale, int32_t max_context_len, void* stream, const NewRows& nr);
+                            float scale, int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                            void* stream, const NewRows& nr);
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

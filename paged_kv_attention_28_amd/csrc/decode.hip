@@ -23,8 +23,8 @@
 //    there are no empty work-groups and no tail of unequal splits. The grid
 //    is one work-group per CU (the launch reserves enough LDS for that), i.e.
 //    one wavefront per SIMD, on 3/4 of the CUs for one or two query heads per
-//    KV head and on all CUs for four or eight (their heavier arithmetic gains
-//    from every CU): fewer, longer ranges than the two per SIMD the registers
+//    KV head and on all CUs for four (its heavier arithmetic gains from every
+//    CU): fewer, longer ranges than the two per SIMD the registers
 //    would allow, which streams faster; each wavefront takes at least 4 steps.
 //    A
 //    wavefront walks its range across sequence boundaries with the loads of
@@ -46,6 +46,9 @@
 //  * Positions past the context end load the last context row (always
 //    written) and get a score of -inf: stale or poisoned cache rows never
 //    enter the result.
+//  * Eight query heads per KV head do eight times the arithmetic of one per
+//    byte, which bounds this kernel's vector FMAs; those calls run on the
+//    MFMA tile form of the prefill kernel instead (decode_tile_call).
 
 #include <mutex>
 
@@ -60,8 +63,6 @@ constexpr int kWavesCap = 4096;    // persistent grid cap (partial slots are siz
 constexpr int kMinStepsPerWave = 4;
 constexpr int kWideMergeMaxSeqs = 32;  // batches up to this size merge per (sequence, head)
 constexpr int kMaxSeqs = 8192;     // LDS scan capacity
-// eight query heads per KV head: from this many (sequence, KV head) pairs on, decode runs on the MFMA tile form
-constexpr int64_t kTileDecodeMinPairs = 512;
 // LDS reserved per stream work-group: more than half a CU's 160 KiB, so each
 // CU holds one work-group (one wavefront per SIMD). On the 256-sequence
 // decode workload this ran 6.5 % faster than two per CU: each wavefront walks
@@ -203,9 +204,9 @@ __device__ __forceinline__ void compute_buf(State<G>& S, const Buf& x, const u32
     }
   }
   if constexpr (LAZY) {
-    // Lazy rescale (eight query heads per KV head, and four over long contexts, where a step's arithmetic
-    // weighs): a head's reference max moves only when a score exceeds it by more than 8 (log2 units), so the
-    // weights stay <= 2^8 and the 16 output multiplies are skipped whenever no lane of the wavefront moves.
+    // Lazy rescale (four query heads per KV head over long contexts, where a step's arithmetic weighs): a
+    // head's reference max moves only when a score exceeds it by more than 8 (log2 units), so the weights
+    // stay <= 2^8 and the 16 output multiplies are skipped whenever no lane of the wavefront moves.
     // For four heads over short contexts (more sequence starts, where the max moves) and for one or two heads
     // (memory-bound) it measured no faster, so those keep the eager form.
 #pragma unroll
@@ -750,7 +751,7 @@ char* scratch_address() {
 
 template <int G, int HKV>
 const void* stream_kernel() {  // occupancy is set by the LDS reservation, the same for both forms
-  return reinterpret_cast<const void*>(&decode_stream_kernel<G, HKV, (G >= 8)>);
+  return reinterpret_cast<const void*>(&decode_stream_kernel<G, HKV, false>);
 }
 
 const void* pick_kernel(int G, int hkv) {
@@ -761,11 +762,10 @@ const void* pick_kernel(int G, int hkv) {
     case 4: return stream_kernel<GG, 4>(); \
     default: return stream_kernel<GG, 8>(); \
   }
-  switch (G) {
+  switch (G) {  // eight query heads per KV head run on the tile form (decode_tile_call)
     case 1: PKV_PICK(1)
     case 2: PKV_PICK(2)
-    case 4: PKV_PICK(4)
-    default: PKV_PICK(8)
+    default: PKV_PICK(4)
   }
 #undef PKV_PICK
 }
@@ -804,6 +804,7 @@ int resident_wgs(const void* kernel, size_t lds) {
 
 bool decode_prepare(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs) {
   if (num_kv_heads < 1 || num_q_heads < num_kv_heads || num_q_heads % num_kv_heads || num_seqs < 1) return false;
+  if (num_q_heads / num_kv_heads == 8) return true;  // the tile form queries nothing
   return resident_wgs(pick_kernel(num_q_heads / num_kv_heads, num_kv_heads), stream_lds(num_seqs)) > 0;
 }
 
@@ -867,21 +868,29 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   }
 
   // Eight query heads per KV head: the row-wide kernel below is bound by its vector arithmetic there
-  // (4.0-4.3 TB/s), so calls with enough (sequence, KV head) pairs for the tile form's one work-group per
-  // pair go to it instead (no workspace, no merge). Measured on MI355X, 64 Q / 8 KV: contexts of 100-2048
-  // tokens from 16 sequences up (37.5 vs 45.2 us at 16, 222 vs 282 us at 256), 4096-32768 tokens from 64
-  // sequences up (972 vs 1061 us; at 32 sequences 781 vs 555 us, a few long pairs set the time).
-  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-  if (G == 8 && (pairs >= kTileDecodeMinPairs || (pairs >= kTileDecodeMinPairs / 4 && max_context_len <= 4096)))
+  // (4.0-4.3 TB/s), so these calls go to the MFMA tile form (split over the keys when the (sequence, KV
+  // head) pairs are too few to fill the GPU). Measured on MI355X, 64 Q / 8 KV, row-wide -> tile form:
+  // 1 sequence of 100-2048 tokens 22.0 -> 13.1 us, 16: 45.8 -> 20.7, 256: 282.5 -> 223.5 us; 4096-32768
+  // tokens, 1 sequence 56.1 -> 45.8 us, 16: 256.2 -> 224.3, 128: 2197 -> 1754 us.
+  if (G == 8) {
+    void* tws = workspace;
+    size_t tws_bytes = workspace_bytes;
+    if (use_scratch) {
+      tws = scratch_address();
+      tws_bytes = kScratchBytes;
+      if (!tws) return fail(PKV_ERR_HIP, "paged_attn_decode_noalloc: cannot find the device's scratch array");
+    }
     return decode_tile_call(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs,
-                            num_q_heads, num_kv_heads, num_blocks, scale, max_context_len, stream, nr);
+                            num_q_heads, num_kv_heads, num_blocks, scale, max_context_len, tws, tws_bytes, stream,
+                            nr);
+  }
 
   const float scale_log2 = scale * 1.4426950408889634f;
   const size_t lds = stream_lds(num_seqs);
   // Part of the CUs, by the query heads per KV head: measured on MI355X (256 CUs) with 192, 224 and 256
   // work-groups, one or two query heads per KV head (a step's arithmetic is light) ran fastest on 192 at
-  // every context length tried (U[100, 2048] to U[4096, 32768]; 2-6 % ahead of 256), four or eight (twice
-  // to four times the arithmetic per byte) on all 256 (5-15 % ahead of 192 at four, 20-25 % at eight).
+  // every context length tried (U[100, 2048] to U[4096, 32768]; 2-6 % ahead of 256), four (twice the
+  // arithmetic per byte) on all 256 (5-15 % ahead of 192).
   const int resident = resident_wgs(pick_kernel(G, num_kv_heads), lds);
   if (resident <= 0) return fail(PKV_ERR_HIP, "paged_attn_decode: cannot query the device");
   const int grid = resident < 8 || G >= 4 ? resident : resident * 3 / 4;
@@ -921,8 +930,8 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
     case 4: PKV_DECODE_LAUNCH(GG, 4, LZ); break;  \
     default: PKV_DECODE_LAUNCH(GG, 8, LZ); break; \
   }
-  // lazy rescale: eight heads per KV head always; four over long contexts (measured: 2.6 % faster on 512
-  // sequences of 4096-32768 tokens, 3.7 % slower on contexts up to 2048)
+  // lazy rescale: four query heads per KV head over long contexts (measured: 2.6 % faster on 512 sequences
+  // of 4096-32768 tokens, 3.7 % slower on contexts up to 2048)
   switch (G) {
     case 1: PKV_DECODE_HKV(1, false) break;
     case 2: PKV_DECODE_HKV(2, false) break;
@@ -933,7 +942,7 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
         PKV_DECODE_HKV(4, false)
       }
       break;
-    default: PKV_DECODE_HKV(8, true) break;
+    default: return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d query heads per KV head", G);
   }
 #undef PKV_DECODE_HKV
 #undef PKV_DECODE_LAUNCH

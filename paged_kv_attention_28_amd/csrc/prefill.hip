@@ -78,6 +78,8 @@ constexpr int kRowsW = kKeysPerTile / 4;    // tile rows each wavefront loads
 constexpr int kRowBytes = kHeadDim * 2;               // one head of one key: 256 B
 constexpr int kTileBytes = kKeysPerTile * kRowBytes;   // a K (or V) tile: 8 KiB, rows unpadded
 constexpr float kNegBig = -1e30f;
+constexpr int kPartStride = 4 + kHeadDim;  // floats per (head, chunk) partial of the split decode form
+constexpr int64_t kTileDecodeTargetWgs = 1536;  // the split decode form's work-group target (2 x 3 per CU x 256)
 constexpr float kRescaleSlack = 8.f;  // log2 units: the reference max moves only when a row max exceeds it by this
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -235,7 +237,8 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const int32_t* __restrict__ cu_seqlens_q,
     const int32_t* __restrict__ context_lens, const char* __restrict__ k_cache, const char* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, int bt_stride, int hq, int hkv, int64_t num_blocks,
-    float scale_log2, int max_q, int max_ctx, const int2* __restrict__ items, int num_seqs, const NewRows nr) {
+    float scale_log2, int max_q, int max_ctx, const int2* __restrict__ items, int num_seqs, const NewRows nr,
+    int chunk_tiles = 0, float* __restrict__ part = nullptr) {
   constexpr int kTokWG = 128 / G;  // query tokens per work-group
   constexpr int kTokW = 32 / G;    // per wavefront
   // K0 V0 K1 V1; after the last tile, the output staging (32 rows per wavefront)
@@ -283,7 +286,15 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
   const int tok_begin = tile * kTokWG;
   const int tok_end = tok_begin + kTokWG < n ? tok_begin + kTokWG : n;
   const int kv_end = c + tok_end;
-  const int nkt = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
+  int nkt = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
+  // decode form split over the keys (chunk_tiles > 0): this work-group takes key tiles [kt0, nkt) of chunk
+  // blockIdx.z and leaves unnormalised partials; chunks past the context have nothing to do
+  int kt0 = 0;
+  if (DECODE && chunk_tiles > 0) {
+    kt0 = (int)blockIdx.z * chunk_tiles;
+    if (kt0 >= nkt) return;
+    nkt = kt0 + chunk_tiles < nkt ? kt0 + chunk_tiles : nkt;
+  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
                      nblk32, wave, gk, gv, kin0 + first * nr.k_stride_b, vin0 + first * nr.v_stride_b, ks, vs);
     }
   };
-  issue(smem, 0, bt[0]);
+  issue(smem, kt0 * kKeysPerTile, bt[(kt0 * kKeysPerTile) >> 8]);
   if (FUSED && (int)threadIdx.x < tok_end - tok_begin) own_slots[threadIdx.x] = my_slot;
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) retire(qreg[kk]);
@@ -540,7 +551,7 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
     __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of the next tile have landed in LDS
     __syncthreads();
   };
-  for (int kt = 0; kt < nkt; kt += 2) {
+  for (int kt = kt0; kt < nkt; kt += 2) {
     key_tile(Stage<0>{}, kt);
     if (kt + 1 < nkt) key_tile(Stage<1>{}, kt + 1);
   }
@@ -549,6 +560,24 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
   // stages its 32 rows in LDS (both tile buffers are free after the last barrier; 8 KiB per
   // wavefront, 16-byte chunks XOR-swizzled by row) and writes whole 256-byte rows.
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (DECODE && chunk_tiles > 0) {
+    // partial of chunk blockIdx.z for the G query heads (rows 0 .. G - 1 of wavefront 0): reference max
+    // (log2 domain), row sum and unnormalised output, [m, l, -, -, o[128]] per head (16-byte aligned rows)
+    if (wave == 0 && col < G) {
+      float* pp = part + ((((int64_t)b * hkv + g) * gridDim.z + blockIdx.z) * G + col) * kPartStride;
+      if (half == 0) {
+        pp[0] = m_ref;
+        pp[1] = l_tot;
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *reinterpret_cast<f32x4*>(pp + 4 + 32 * dt + 8 * rq + 4 * half) =
+              f32x4{acc_o[dt][4 * rq + 0], acc_o[dt][4 * rq + 1], acc_o[dt][4 * rq + 2], acc_o[dt][4 * rq + 3]};
+    }
+    return;
+  }
   if (wave_live) {
     const float inv = 1.f / l_tot;
     char* stage = smem + wave * (32 * kRowBytes);
@@ -576,6 +605,66 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
       }
     }
   }
+}
+
+// Merge of the split decode form: out[s, h] = sum_c 2^(m_c - M) o_c / sum_c 2^(m_c - M) l_c over the chunks
+// c of sequence s's context that hold keys (M = max_c m_c, the partials' reference maxima in log2 units),
+// in chunk order; zero rows for an empty context. One work-group per sequence, 16 lanes of 8 dims per query
+// head; the chunks' partials are loaded eight at a time before they are combined.
+template <int G>
+__global__ __launch_bounds__(1024) void decode_tile_merge_kernel(uint16_t* __restrict__ out,
+                                                                 const float* __restrict__ part,
+                                                                 const int32_t* __restrict__ context_lens, int hq,
+                                                                 int hkv, int max_ctx, int chunks, int chunk_tiles) {
+  constexpr int kBatch = 8;
+  const int b = blockIdx.x;
+  const int h = (int)threadIdx.x >> 4;
+  const int d0 = 8 * (threadIdx.x & 15);
+  int L = context_lens[b];
+  L = L > max_ctx ? max_ctx : L;
+  u32x4* op = reinterpret_cast<u32x4*>(out + ((int64_t)b * hq + h) * kHeadDim + d0);
+  if (L <= 0) {
+    *op = u32x4{0u, 0u, 0u, 0u};
+    return;
+  }
+  const int nkt = (L + kKeysPerTile - 1) / kKeysPerTile;
+  const int nc = (nkt + chunk_tiles - 1) / chunk_tiles;  // chunks that hold keys
+  const int g = h / G;
+  const float* base = part + (((int64_t)b * hkv + g) * chunks * G + h % G) * kPartStride;
+  float M = kNegBig, lsum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nc; c0 += kBatch) {
+    float m2[kBatch], l2[kBatch];
+    f32x4 lo[kBatch], hi[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = c0 + k < nc ? c0 + k : nc - 1;
+      const float* pp = base + (int64_t)c * G * kPartStride;
+      m2[k] = pp[0];
+      l2[k] = pp[1];
+      lo[k] = *reinterpret_cast<const f32x4*>(pp + 4 + d0);
+      hi[k] = *reinterpret_cast<const f32x4*>(pp + 4 + d0 + 4);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (c0 + k >= nc) break;
+      const float mn = fmaxf(M, m2[k]);
+      const float fa = __builtin_amdgcn_exp2f(M - mn);
+      const float fb = __builtin_amdgcn_exp2f(m2[k] - mn);
+      lsum = lsum * fa + l2[k] * fb;
+      const float a2[8] = {lo[k].x, lo[k].y, lo[k].z, lo[k].w, hi[k].x, hi[k].y, hi[k].z, hi[k].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * fa + a2[e] * fb;
+      M = mn;
+    }
+  }
+  const float inv = 1.f / lsum;
+  u32x4 w;
+  w.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  w.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  w.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  w.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *op = w;
 }
 
 }  // namespace
@@ -661,27 +750,57 @@ namespace pkv {
 pkv_status decode_tile_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                             const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int64_t num_blocks,
-                            float scale, int32_t max_context_len, void* stream, const NewRows& nr) {
-  if (num_q_heads != 8 * num_kv_heads)
+                            float scale, int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                            void* stream, const NewRows& nr) {
+  constexpr int G = 8;
+  if (num_q_heads != G * num_kv_heads)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: the tile form takes 8 query heads per KV head");
   if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: more than 65535 sequences");
   if (num_seqs == 0) return ok();
+  // Split over the keys when the (sequence, KV head) pairs alone would leave the GPU short of work-groups:
+  // up to 16 chunks of at least 4 tiles each, aiming at about twice the resident work-groups (three per CU).
+  const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+  const int max_tiles = (max_context_len + kKeysPerTile - 1) / kKeysPerTile;
+  int chunks = 1;
+  if (pairs < kTileDecodeTargetWgs) {
+    chunks = (int)((kTileDecodeTargetWgs + pairs - 1) / pairs);
+    chunks = chunks < 16 ? chunks : 16;
+    const int by_len = max_tiles / 4 > 1 ? max_tiles / 4 : 1;
+    chunks = chunks < by_len ? chunks : by_len;
+  }
+  int chunk_tiles = 0;
+  float* part = nullptr;
+  if (chunks > 1) {
+    chunk_tiles = (max_tiles + chunks - 1) / chunks;
+    chunks = (max_tiles + chunk_tiles - 1) / chunk_tiles;
+    const size_t need = (size_t)pairs * chunks * G * kPartStride * sizeof(float);
+    if (workspace && need <= workspace_bytes && !(reinterpret_cast<uintptr_t>(workspace) & 15)) {
+      part = static_cast<float*>(workspace);
+    } else {  // not enough workspace for the partials: one work-group per pair
+      chunks = 1;
+      chunk_tiles = 0;
+    }
+  }
   const float scale_log2 = scale * 1.4426950408889634f;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid(num_kv_heads, num_seqs);
+  const dim3 grid(num_kv_heads, num_seqs, chunks);
   uint16_t* o = static_cast<uint16_t*>(out);
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const char* kc = static_cast<const char*>(k_cache);
   const char* vc = static_cast<const char*>(v_cache);
   if (nr.k)
-    hipLaunchKernelGGL((prefill_kernel<8, true, true>), grid, dim3(256), 0, s, o, qq, nullptr, context_lens, kc, vc,
+    hipLaunchKernelGGL((prefill_kernel<G, true, true>), grid, dim3(256), 0, s, o, qq, nullptr, context_lens, kc, vc,
                        block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2, 1,
-                       max_context_len, nullptr, num_seqs, nr);
+                       max_context_len, nullptr, num_seqs, nr, chunk_tiles, part);
   else
-    hipLaunchKernelGGL((prefill_kernel<8, false, true>), grid, dim3(256), 0, s, o, qq, nullptr, context_lens, kc,
+    hipLaunchKernelGGL((prefill_kernel<G, false, true>), grid, dim3(256), 0, s, o, qq, nullptr, context_lens, kc,
                        vc, block_tables, block_table_stride, num_q_heads, num_kv_heads, num_blocks, scale_log2, 1,
-                       max_context_len, nullptr, num_seqs, nr);
-  return check_launch("paged_attn_decode (tile form)");
+                       max_context_len, nullptr, num_seqs, nr, chunk_tiles, part);
+  pkv_status st = check_launch("paged_attn_decode (tile form)");
+  if (st != PKV_OK || chunks == 1) return st;
+  hipLaunchKernelGGL((decode_tile_merge_kernel<G>), dim3(num_seqs), dim3(num_q_heads * 16), 0, s, o, part,
+                     context_lens, num_q_heads, num_kv_heads, max_context_len, chunks, chunk_tiles);
+  return check_launch("paged_attn_decode (tile form merge)");
 }
 
 }  // namespace pkv

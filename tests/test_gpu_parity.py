@@ -254,9 +254,9 @@ EDGE = {
     "decode_hkv4_gqa4_long": _dec([5000, 4097, 100], hq=16, hkv=4, **PEAKY),
     "prefill_hkv4_gqa2": dict(lens=[300, 129, 1000], cached=[0, 100, 511], hq=8, hkv=4),
     "prefill_hkv4_gqa4": dict(lens=[257, 700], cached=[0, 256], hq=16, hkv=4),
-    # eight query heads per KV head on enough (sequence, KV head) pairs: the MFMA tile form of decode
-    # (contexts up to 4096 from 16 sequences, longer from 64), with its empty-context rows, one-token
-    # contexts, peaky and rising scores
+    # eight query heads per KV head: the MFMA tile form of decode, one work-group per (sequence, KV head)
+    # when the pairs fill the GPU, else split over the keys and merged (every G = 8 case above and below),
+    # with its empty-context rows, one-token contexts, peaky and rising scores, long single contexts
     "decode_tile_gqa8": _dec([(61 * i) % 2100 + 1 for i in range(24)], hq=64),
     "decode_tile_gqa8_pad": dict(lens=[1, 1, 2, 700] + [(37 * i) % 500 + 3 for i in range(14)],
                                  cached=[0, 0, 1, 699] + [(37 * i) % 500 + 2 for i in range(14)], hq=64,
@@ -264,6 +264,9 @@ EDGE = {
     "decode_tile_gqa8_long": _dec([(97 * i) % 600 + 1 for i in range(60)] + [4200, 5000, 4097, 6100], hq=64),
     "decode_tile_gqa8_peaky": _dec([(53 * i) % 1800 + 1 for i in range(20)], hq=64, **PEAKY),
     "decode_tile_gqa8_ramp": _dec([(71 * i) % 3000 + 1 for i in range(20)], hq=64, **RAMP),
+    "decode_tile_split_one_long": _dec([40000], hq=64),
+    "decode_tile_split_few": _dec([9000, 300, 1, 12000], hq=64, **PEAKY),
+    "decode_tile_split_hkv1": _dec([5, 2500, 777], hq=8, hkv=1),
     # more than 32 sequences with 8 and 4 query heads: the per-sequence (serial) merge
     "decode_hq8_hkv4_40seqs": _dec([(41 * i) % 900 + 1 for i in range(40)], hq=8, hkv=4),
     "decode_hq4_hkv1_40seqs": _dec([(29 * i) % 1300 + 1 for i in range(40)], hq=4, hkv=1),
@@ -330,7 +333,7 @@ def _random_case(seed: int) -> dict:
 @pytest.mark.parametrize("seed", range(16))
 def test_random_shapes_parity(seed):
     """Seeded random shapes (every G and KV-head count, ragged batches, cached prefixes, padding rows, wider
-    scores) against the oracle; decode calls that fit the MFMA tile form's rule take it."""
+    scores) against the oracle; decode with eight query heads per KV head runs on the MFMA tile form."""
     case = _random_case(seed)
     print(f"[random] seed {seed}: {case['kind']} {len(case['lens'])} seqs, {case['hq']}Q/{case['hkv']}KV, "
           f"max len {max(case['lens'])}, q x {case['q_mult']}", flush=True)
@@ -348,7 +351,7 @@ def test_random_shapes_parity(seed):
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
                "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
                "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs", "decode_tile_gqa8_pad",
-               "decode_tile_gqa8_long"]
+               "decode_tile_gqa8_long", "decode_tile_split_few", "decode_tile_split_hkv1"]
 
 
 @pytest.mark.parametrize("case", FUSED_CASES)
@@ -636,8 +639,8 @@ def test_decode_graphs_replay_matches_eager(hq):
     of the eager kv_store and paged_attn_decode calls on the same static buffers, for batches that hit an exact
     bucket and batches that need padding rows; each graph is replayed three
     times with unrelated eager work and synchronisation in between, and the
-    real rows are also checked against the oracle. With 64 query heads (8 per KV head) the buckets of 16
-    rows and up run the MFMA tile form of decode, the smaller ones the row-wide kernel."""
+    real rows are also checked against the oracle. With 64 query heads (8 per KV head) every bucket runs the
+    MFMA tile form of decode, split over the keys with a merge below 192 rows."""
     import paged_kv_attention_28_amd as P
     rng = np.random.default_rng(31)
     lens = [int(x) for x in rng.integers(1, 1500, size=64)]

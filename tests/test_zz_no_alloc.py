@@ -2,8 +2,11 @@
 array, for callers that cannot allocate) against paged_attn_decode with a
 caller workspace: identical bits on two calls in a row, the second with a
 smaller batch (the scratch then still holds the first call's partials), and
-the oracle on the first; launches needing more than the scratch are
-rejected on the host."""
+the oracle on both; with 64 query heads (eight per KV head) both calls run
+on the MFMA tile form, the second one split over the keys with its partials
+in the scratch. (A launch needing more than the scratch is rejected on the
+host; on a 256-CU GPU no supported shape does: the row-wide kernel needs at
+most about 34 MB with 32 query heads, the tile form's partials about 6.5 MB.)"""
 
 from __future__ import annotations
 
@@ -40,7 +43,7 @@ def _both(w, dw, q, m):
     return ref, got
 
 
-@pytest.mark.parametrize("hq", [16, 32])
+@pytest.mark.parametrize("hq", [16, 32, 64])
 def test_noalloc_matches_workspace_call_twice(hq):
     rng = np.random.default_rng(60 + hq)
     big = [int(x) for x in rng.integers(1, 3000, size=300)]
@@ -59,16 +62,3 @@ def test_noalloc_matches_workspace_call_twice(hq):
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), "second (smaller) call differs"
     kc, vc = O.build_caches(w, device="cuda")
     assert_close(got, O.run_pass(w, p, kc, vc, q=q), None, f"noalloc H_q {hq}, small batch")
-
-
-def test_noalloc_rejects_launches_beyond_its_scratch():
-    """64 query heads on every resident wavefront need about 68 MB of partials: rejected before any launch,
-    and the output is left as it was."""
-    w, dw, p, q, m = _decode_case([300, 5], 64, seed=63)
-    out = torch.full_like(q, 3.0)
-    with pytest.raises(B.PkvError) as e:
-        B.paged_attn_decode_noalloc(out, q, dw.k_cache, dw.v_cache, m.block_tables, m.context_lens, w.scale,
-                                    m.max_context_len)
-    assert e.value.status == 2 and "scratch" in str(e.value)
-    torch.cuda.synchronize()
-    assert (out.float() == 3.0).all()
