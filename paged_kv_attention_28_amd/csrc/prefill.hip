@@ -747,16 +747,14 @@ pkv_status prefill_call(void* out, const void* q, const int32_t* cu_seqlens_q, c
 
 namespace pkv {
 
-pkv_status decode_tile_call(void* out, const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
-                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int64_t num_blocks,
-                            float scale, int32_t max_context_len, void* workspace, size_t workspace_bytes,
-                            void* stream, const NewRows& nr) {
-  constexpr int G = 8;
-  if (num_q_heads != G * num_kv_heads)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: the tile form takes 8 query heads per KV head");
-  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: more than 65535 sequences");
-  if (num_seqs == 0) return ok();
+namespace {
+
+template <int G>
+pkv_status decode_tile_launch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int64_t num_blocks,
+                              float scale, int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                              void* stream, const NewRows& nr) {
   // Split over the keys when the (sequence, KV head) pairs alone would leave the GPU short of work-groups:
   // up to 16 chunks of at least 4 tiles each, aiming at about twice the resident work-groups (three per CU).
   const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
@@ -801,6 +799,31 @@ pkv_status decode_tile_call(void* out, const void* q, const void* k_cache, const
   hipLaunchKernelGGL((decode_tile_merge_kernel<G>), dim3(num_seqs), dim3(num_q_heads * 16), 0, s, o, part,
                      context_lens, num_q_heads, num_kv_heads, max_context_len, chunks, chunk_tiles);
   return check_launch("paged_attn_decode (tile form merge)");
+}
+
+}  // namespace
+
+pkv_status decode_tile_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int64_t num_blocks,
+                            float scale, int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                            void* stream, const NewRows& nr) {
+  if (num_kv_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: head counts %d/%d unsupported", num_q_heads, num_kv_heads);
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: more than 65535 sequences");
+  if (num_seqs == 0) return ok();
+#define PKV_TILE_DECODE(GG)                                                                                       \
+  return decode_tile_launch<GG>(out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs, \
+                                num_q_heads, num_kv_heads, num_blocks, scale, max_context_len, workspace,          \
+                                workspace_bytes, stream, nr)
+  switch (num_q_heads / num_kv_heads) {
+    case 2: PKV_TILE_DECODE(2);
+    case 4: PKV_TILE_DECODE(4);
+    case 8: PKV_TILE_DECODE(8);
+    default:
+      return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: the tile form takes 2, 4 or 8 query heads per KV head");
+  }
+#undef PKV_TILE_DECODE
 }
 
 }  // namespace pkv

@@ -330,12 +330,17 @@ def _random_case(seed: int) -> dict:
     return dict(lens=lens, cached=cached, hq=hq, hkv=hkv, kind="prefill", q_mult=q_mult, seed=seed)
 
 
+@pytest.mark.parametrize("form", ["auto", "rowwide"])
 @pytest.mark.parametrize("seed", range(16))
-def test_random_shapes_parity(seed):
+def test_random_shapes_parity(seed, form, monkeypatch):
     """Seeded random shapes (every G and KV-head count, ragged batches, cached prefixes, padding rows, wider
     scores) against the oracle; decode with eight query heads per KV head runs on the MFMA tile form."""
     case = _random_case(seed)
-    print(f"[random] seed {seed}: {case['kind']} {len(case['lens'])} seqs, {case['hq']}Q/{case['hkv']}KV, "
+    if form != "auto":
+        if case["kind"] != "decode" or _g(case) not in (2, 4):
+            pytest.skip("one decode form only: prefill, or one or eight query heads per KV head")
+        monkeypatch.setenv("PKV_DECODE_FORM", form)
+    print(f"[random] seed {seed} ({form}): {case['kind']} {len(case['lens'])} seqs, {case['hq']}Q/{case['hkv']}KV, "
           f"max len {max(case['lens'])}, q x {case['q_mult']}", flush=True)
     w = custom(**case)
     dw = H.DeviceWorkload(w).build()
@@ -348,16 +353,45 @@ def test_random_shapes_parity(seed):
     assert_close(out, ref, m.host.cu_seqlens_q, f"random seed {seed}")
 
 
+def _g(case: dict) -> int:
+    return case.get("hq", 16) // case.get("hkv", 8)
+
+
+# decode cases with two or four query heads per KV head, which either decode form can take
+DECODE_FORM_CASES = sorted(n for n, c in EDGE.items() if c.get("kind") == "decode" and _g(c) in (2, 4))
+
+
+@pytest.mark.parametrize("form", ["rowwide", "tile"])
+@pytest.mark.parametrize("name", DECODE_FORM_CASES)
+def test_decode_forms_parity(name, form, monkeypatch):
+    """Every decode edge case with two or four query heads per KV head in both decode forms (the row-wide
+    stream-K kernel and the MFMA tile form, forced with PKV_DECODE_FORM) against the oracle."""
+    monkeypatch.setenv("PKV_DECODE_FORM", form)
+    w = custom(**EDGE[name])
+    dw = H.DeviceWorkload(w).build()
+    kc, vc = O.build_caches(w, device="cuda")
+    p = w.passes[0]
+    q, m = dw.pass_inputs(p)
+    out = dw.run_pass(p, q, m)
+    ref = O.run_pass(w, p, kc, vc, q=q)
+    assert_close(out, ref, m.host.cu_seqlens_q, f"{name} ({form})")
+    if name == "decode_pad_rows":
+        assert (_f64(out[2:]) == 0).all()
+
+
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
                "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
                "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs", "decode_tile_gqa8_pad",
                "decode_tile_gqa8_long", "decode_tile_split_few", "decode_tile_split_hkv1"]
 
 
+@pytest.mark.parametrize("form", ["auto", "rowwide"])
 @pytest.mark.parametrize("case", FUSED_CASES)
-def test_decode_store_fused_matches_two_calls(case):
+def test_decode_store_fused_matches_two_calls(case, form, monkeypatch):
     """paged_attn_decode_store (new token read from its input row and stored by the wavefront that
     reads it) gives the bits of kv_store followed by paged_attn_decode: outputs and both caches."""
+    if form != "auto":
+        monkeypatch.setenv("PKV_DECODE_FORM", form)
     from paged_kv_attention_28_amd import binding as B
     w = W.make(2) if case == "config2" else custom(**EDGE[case])
     p = w.passes[0]
@@ -633,14 +667,16 @@ def test_binding_launches_on_current_stream():
     assert torch.equal(kflat[rows].view(torch.int16), key.view(torch.int16))
 
 
-@pytest.mark.parametrize("hq", [16, 64])
-def test_decode_graphs_replay_matches_eager(hq):
+@pytest.mark.parametrize("hq,form", [(16, "auto"), (16, "rowwide"), (64, "auto")])
+def test_decode_graphs_replay_matches_eager(hq, form, monkeypatch):
     """Decode-step graphs (the fused store + decode per bucket) give the bits
     of the eager kv_store and paged_attn_decode calls on the same static buffers, for batches that hit an exact
     bucket and batches that need padding rows; each graph is replayed three
     times with unrelated eager work and synchronisation in between, and the
-    real rows are also checked against the oracle. With 64 query heads (8 per KV head) every bucket runs the
-    MFMA tile form of decode, split over the keys with a merge below 192 rows."""
+    real rows are also checked against the oracle. These batches are small enough for the MFMA tile form of
+    decode (split over the keys with a merge); with 16 query heads they also run in the row-wide form."""
+    if form != "auto":
+        monkeypatch.setenv("PKV_DECODE_FORM", form)
     import paged_kv_attention_28_amd as P
     rng = np.random.default_rng(31)
     lens = [int(x) for x in rng.integers(1, 1500, size=64)]
@@ -695,10 +731,13 @@ def test_decode_graphs_replay_matches_eager(hq):
     graphs.close()
 
 
-def test_decode_step_graphs_all_layers_match_eager():
+@pytest.mark.parametrize("form", ["auto", "rowwide"])
+def test_decode_step_graphs_all_layers_match_eager(form, monkeypatch):
     """Graphs holding a whole decode step of several layers (each layer's fused store + decode, one replay per
     step) give every layer's eager bits on the same buffers, for exact and padded buckets, three replays each
     with unrelated eager work in between; layer outputs and caches also match the oracle."""
+    if form != "auto":
+        monkeypatch.setenv("PKV_DECODE_FORM", form)
     import paged_kv_attention_28_amd as P
     rng = np.random.default_rng(33)
     lens = [int(x) for x in rng.integers(1, 1200, size=48)]
