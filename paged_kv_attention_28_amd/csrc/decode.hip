@@ -65,8 +65,11 @@ constexpr int kWavesCap = 4096;    // persistent grid cap (partial slots are siz
 constexpr int kMinStepsPerWave = 4;
 constexpr int kWideMergeMaxSeqs = 32;  // batches up to this size merge per (sequence, head)
 constexpr int kMaxSeqs = 8192;     // LDS scan capacity
-// two or four query heads per KV head: calls with num_seqs x max_context_len up to this take the tile form
-constexpr int64_t kTileDecodeMaxTokens = 1 << 17;
+// two or four query heads per KV head: calls of up to kTileFewSeqs sequences, or of up to kTileShortSeqs
+// sequences with max_context_len up to kTileShortCtx, take the tile form
+constexpr int kTileFewSeqs = 4;
+constexpr int kTileShortSeqs = 48;
+constexpr int kTileShortCtx = 1024;
 // LDS reserved per stream work-group: more than half a CU's 160 KiB, so each
 // CU holds one work-group (one wavefront per SIMD). On the 256-sequence
 // decode workload this ran 6.5 % faster than two per CU: each wavefront walks
@@ -873,19 +876,19 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
 
   // The MFMA tile form (decode_tile_call) takes eight query heads per KV head, where the row-wide kernel
   // below is bound by its vector arithmetic (4.0-4.3 TB/s), and small calls with two or four, where the
-  // row-wide kernel's fixed cost (two launches, a merge over pieces spread across all wavefronts) dominates:
-  // num_seqs x max_context_len (a bound on the call's tokens) up to 2^17. Measured on MI355X, row-wide ->
-  // tile form: 64 Q / 8 KV, 1 sequence of 100-2048 tokens 22.0 -> 13.1 us, 16: 45.8 -> 20.7, 256: 282.5 ->
-  // 223.5 us, 4096-32768 tokens, 1 sequence 56.1 -> 45.8 us, 128: 2197 -> 1754 us; 16 Q / 8 KV, 100-1024
-  // tokens, 1 sequence 11.7 -> 10.1 us, 16: 17.6 -> 12.3, 32: 25.8 -> 20.3, 128: 54.4 -> 52.4 us, but 256 of
-  // 100-2048 tokens 176.6 -> 216.4 us and 16 of 4096-32768 150.4 -> 219.5 us; 32 Q / 8 KV alike.
+  // row-wide kernel's fixed cost (two launches, a merge over pieces spread across all wavefronts) dominates.
+  // Measured on MI355X, 64 Q / 8 KV, row-wide -> tile form: 1 sequence of 100-2048 tokens 22.0 -> 13.1 us,
+  // 16: 45.8 -> 20.7, 256: 282.5 -> 223.5 us; 4096-32768 tokens, 1 sequence 56.1 -> 45.8 us, 128: 2197 -> 1754
+  // us. 16 Q / 8 KV, a 28-layer decode step with the store fused, each layer its own caches: contexts of
+  // 100-1024 tokens, 16-48 sequences 5-10 % faster on the tile form, 64 sequences 6 % slower; contexts of
+  // 1024-2048 tokens, 8-64 sequences 5-17 % slower; 1-4 sequences of any length level or faster.
   // PKV_DECODE_FORM=tile or =rowwide in the environment overrides the choice for two or four query heads
   // per KV head (read on every call; for tests and tuning)
   const char* form = getenv("PKV_DECODE_FORM");
   const bool force_tile = form && !strcmp(form, "tile");
   const bool force_rowwide = form && !strcmp(form, "rowwide");
-  if (G == 8 || (G >= 2 && !force_rowwide &&
-                 (force_tile || (int64_t)num_seqs * max_context_len <= kTileDecodeMaxTokens))) {
+  const bool small_call = num_seqs <= kTileFewSeqs || (num_seqs <= kTileShortSeqs && max_context_len <= kTileShortCtx);
+  if (G == 8 || (G >= 2 && !force_rowwide && (force_tile || small_call))) {
     void* tws = workspace;
     size_t tws_bytes = workspace_bytes;
     if (use_scratch) {
