@@ -64,7 +64,8 @@
 //  * The output leaves through LDS: the accumulators hold O^T (a lane owns one
 //    query row, 8-byte runs of dims), so each wavefront stages its 32 rows in
 //    LDS and writes whole 256-byte rows, 16 bytes per lane; stored directly,
-//    every store instruction would touch 32 rows 16 bytes at a time.
+//    every store instruction would touch 32 rows 16 bytes at a time. The row
+//    stores are nontemporal (streaming).
 
 #include "common.h"
 
@@ -601,7 +602,9 @@ __global__ __launch_bounds__(256, kKeysPerTile == 32 ? 3 : 2) void prefill_kerne
       const int t = tok_begin + rw / G;
       if (t < tok_end) {
         uint16_t* op = out + ((int64_t)(q0 + t) * hq + g * G + (rw % G)) * kHeadDim + 8 * p;
-        *reinterpret_cast<u32x4*>(op) = v;
+        // streaming store: nothing in this launch reads the output, so it should not evict the K/V
+        // lines that other query tiles of the sequence are about to reuse from L2
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(op));
       }
     }
   }
