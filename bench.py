@@ -369,7 +369,7 @@ def cold_warm(torch, runner, call_bytes: int, reps: int = 50) -> dict:
     and are full of dirty lines, as after a large GEMM). Medians in microseconds, and fractions of HBM peak."""
     flush = torch.empty(2**30 // 4, dtype=torch.int32, device=runner.q.device)
     out = {}
-    for mode in ("warm", "cold"):
+    for mode in ("cold", "warm"):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
         runner.fused_only()
         for i, e in enumerate(ev):
@@ -445,7 +445,7 @@ def copy_ceiling(torch, dev, reps: int = 10) -> dict:
 
 def back_to_back(torch, runner, seconds: float = 0.1) -> float:
     """Mean time of the attention call launched back to back for about `seconds` (the GPU never idles, so the
-    shader clock settles), after the timed steps."""
+    shader clock settles), on the metadata the runner last uploaded."""
     runner.attention_only()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -826,15 +826,19 @@ def main():
     runner = H.StepRunner(dw, wd.passes[0])
     db = decode_bytes(wd)
     step_bytes = db["attn"] + db["store"]
+    # the untimed cold/warm medians run first: right after the setup stores the GPU needs a few dozen calls to
+    # settle (calls inside the first steps ran about 7 % slower), which the W warm-up steps alone do not cover
+    runner.prepare_and_upload()
+    torch.cuda.synchronize()
+    cw = cold_warm(torch, runner, db["fused_call"])
+    log(f"[bench] decode call, median of 50: warm {cw['warm']:.1f} us ({cw['warm_frac']:.1%}), cold (1 GiB written "
+        f"before each call) {cw['cold']:.1f} us ({cw['cold_frac']:.1%})")
     ms, call_ms = fused_steps(runner, args.steps, args.warmup, torch)
     value = step_bytes / (ms * 1e-3) / 1e9
     call_avg = float(call_ms.mean())
     achieved = db["fused_call"] / (call_avg * 1e-3) / 1e9
     log(f"[bench] decode step {ms * 1e3:.1f} us wall -> {value:.0f} GB/s; paged_attn_decode_store call "
         f"{call_avg * 1e3:.1f} us -> {achieved:.0f} GB/s ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
-    cw = cold_warm(torch, runner, db["fused_call"])
-    log(f"[bench] decode call, median of 50: warm {cw['warm']:.1f} us ({cw['warm_frac']:.1%}), cold (1 GiB written "
-        f"before each call) {cw['cold']:.1f} us ({cw['cold_frac']:.1%})")
     two = None
     if not args.no_fused:
         tms, store_ms, attn_ms = time_steps(runner, args.steps, args.warmup, torch)
@@ -857,6 +861,9 @@ def main():
         dwp.run_setup()
         torch.cuda.synchronize()
         rp = H.StepRunner(dwp, wp.passes[0])
+        rp.prepare_and_upload()
+        torch.cuda.synchronize()
+        b2b = None if args.no_back_to_back else back_to_back(torch, rp)  # untimed for the step; also settles the GPU
         pms, pstore, pattn = time_steps(rp, max(args.steps // 2, 5), args.warmup, torch)
         pav = float(pattn.mean())
         tflops = pw["flops"] / (pav * 1e-3) / 1e12
@@ -871,14 +878,13 @@ def main():
             f"({pw['bytes'] / 1e9:.3f} GB: q + out + {pw['kv_rows']} distinct K/V rows) -> "
             f"max / t = {roof:.1%}")
         b2b_line = None
-        if not args.no_back_to_back:
-            b2b = back_to_back(torch, rp)
+        if b2b is not None:
             b2b_tflops = pw["flops"] / (b2b * 1e-3) / 1e12
             log(f"[bench] prefill attention back to back for 0.1 s: {b2b * 1e3:.1f} us -> {b2b_tflops:.1f} "
                 f"TFLOP/s ({b2b_tflops / BF16_PEAK_TFLOPS:.1%})")
             b2b_line = {"attn_us": round(b2b * 1e3, 2), "tflops": round(b2b_tflops, 2),
                         "pct_bf16_peak": round(100 * b2b_tflops / BF16_PEAK_TFLOPS, 2),
-                        "note": "the same call launched back to back for 0.1 s after the timed steps"}
+                        "note": "the same call launched back to back for 0.1 s (before the timed steps)"}
         fpms, fpcall = fused_steps(rp, max(args.steps // 2, 5), args.warmup, torch)
         fpav = float(fpcall.mean())
         fused_line = {"step_us_wall": round(fpms * 1e3, 2), "call_us": round(fpav * 1e3, 2),
