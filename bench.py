@@ -864,7 +864,10 @@ def main():
         rp.prepare_and_upload()
         torch.cuda.synchronize()
         b2b = None if args.no_back_to_back else back_to_back(torch, rp)  # untimed for the step; also settles the GPU
-        pms, pstore, pattn = time_steps(rp, max(args.steps // 2, 5), args.warmup, torch)
+        # 30 timed steps at least: a prefill call is short (70-80 us) and its time moves with the shader clock,
+        # which the first steps after a pause still ramp up
+        psteps = max(args.steps, 30)
+        pms, pstore, pattn = time_steps(rp, psteps, max(args.warmup, 10), torch)
         pav = float(pattn.mean())
         tflops = pw["flops"] / (pav * 1e-3) / 1e12
         store_gbs = pw["store"] / (float(pstore.mean()) * 1e-3) / 1e9
@@ -885,7 +888,7 @@ def main():
             b2b_line = {"attn_us": round(b2b * 1e3, 2), "tflops": round(b2b_tflops, 2),
                         "pct_bf16_peak": round(100 * b2b_tflops / BF16_PEAK_TFLOPS, 2),
                         "note": "the same call launched back to back for 0.1 s (before the timed steps)"}
-        fpms, fpcall = fused_steps(rp, max(args.steps // 2, 5), args.warmup, torch)
+        fpms, fpcall = fused_steps(rp, psteps, max(args.warmup, 10), torch)
         fpav = float(fpcall.mean())
         fused_line = {"step_us_wall": round(fpms * 1e3, 2), "call_us": round(fpav * 1e3, 2),
                       "tflops": round(pw["flops"] / (fpav * 1e-3) / 1e12, 2),
@@ -899,7 +902,7 @@ def main():
                                "about half with a shared 256/512-token cached prefix, first seq a mid-block chunk "
                                "continuation; 16Q/8KV, d128, bf16, block 256",
                    "tflops": round(tflops, 2), "pct_bf16_peak": round(100 * tflops / BF16_PEAK_TFLOPS, 2),
-                   "attn_us": round(pav * 1e3, 2), "step_us_wall": round(pms * 1e3, 2),
+                   "attn_us": round(pav * 1e3, 2), "step_us_wall": round(pms * 1e3, 2), "timed_steps": psteps,
                    "store_us": round(float(pstore.mean()) * 1e3, 2), "store_gbs": round(store_gbs, 1),
                    "flops": pw["flops"], "pairs": pw["pairs"], "bytes": pw["bytes"],
                    "t_mfma_us": round(t_mfma * 1e6, 2), "t_hbm_us": round(t_hbm * 1e6, 2),

@@ -180,7 +180,13 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * sequence, key chunk) with up to 16 chunks of at least 4 x 32 keys, whose
  * partials (at most about 6.5 MB) go to the workspace and are merged by a
  * second kernel in chunk order; the chunking depends only on num_seqs,
- * num_kv_heads and max_context_len.
+ * num_kv_heads and max_context_len. Two or four query heads per KV head take
+ * the same tile kernel for small calls (num_seqs <= 4, or num_seqs <= 48 with
+ * max_context_len <= 1024), the stream-K kernel otherwise; the environment
+ * variable PKV_DECODE_FORM=tile or =rowwide, read on every call, forces one
+ * of the two for two or four query heads per KV head (tests, tuning). The
+ * two forms round differently (the tile form's weights are bf16), so their
+ * outputs differ within the attention tolerance, not bit for bit.
  */
 pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const int32_t* block_tables, int32_t block_table_stride,
