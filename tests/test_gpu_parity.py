@@ -379,6 +379,50 @@ def test_decode_forms_parity(name, form, monkeypatch):
         assert (_f64(out[2:]) == 0).all()
 
 
+def _boundary(n, hi, hq, seed):
+    """n decode sequences of U[2, hi] tokens, the longest exactly hi (so max_context_len == hi)."""
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(2, hi + 1, size=n - 1)] + [hi]
+    return _dec(lens, hq=hq, hkv=8, seed=seed)
+
+
+# calls on both sides of the rule that sends two or four query heads per KV head to the tile form (at most 4
+# sequences, or at most 48 with max_context_len <= 1024): name -> (case, form the default dispatch must take)
+DISPATCH_CASES = {
+    "g2_4seqs_2048": (_boundary(4, 2048, 16, 41), "tile"),
+    "g2_5seqs_2048": (_boundary(5, 2048, 16, 42), "rowwide"),
+    "g2_48seqs_1024": (_boundary(48, 1024, 16, 43), "tile"),
+    "g2_49seqs_1024": (_boundary(49, 1024, 16, 44), "rowwide"),
+    "g2_48seqs_1025": (_boundary(48, 1025, 16, 45), "rowwide"),
+    "g4_4seqs_4096": (_boundary(4, 4096, 32, 46), "tile"),
+    "g4_48seqs_1024": (_boundary(48, 1024, 32, 47), "tile"),
+    "g4_49seqs_1024": (_boundary(49, 1024, 32, 48), "rowwide"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DISPATCH_CASES))
+def test_decode_dispatch_boundaries(name, monkeypatch):
+    """At each boundary of the decode form rule the default call gives exactly the bits of the form the rule
+    names (the two forms round differently, so their bits tell them apart), and matches the oracle."""
+    case, expect = DISPATCH_CASES[name]
+    w = custom(**case)
+    dw = H.DeviceWorkload(w).build()
+    kc, vc = O.build_caches(w, device="cuda")
+    p = w.passes[0]
+    q, m = dw.pass_inputs(p)
+    outs = {}
+    for form in ("auto", "tile", "rowwide"):
+        monkeypatch.setenv("PKV_DECODE_FORM", form)
+        outs[form] = dw.run_pass(p, q, m).clone()
+    monkeypatch.delenv("PKV_DECODE_FORM")
+    other = "rowwide" if expect == "tile" else "tile"
+    assert torch.equal(outs["auto"].view(torch.int16), outs[expect].view(torch.int16)), f"{name}: not the {expect} form"
+    assert not torch.equal(outs[expect].view(torch.int16), outs[other].view(torch.int16)), f"{name}: forms agree bit for bit"
+    ref = O.run_pass(w, p, kc, vc, q=q)
+    for form, out in outs.items():
+        assert_close(out, ref, m.host.cu_seqlens_q, f"{name} ({form})")
+
+
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
                "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
                "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs", "decode_tile_gqa8_pad",
