@@ -24,8 +24,8 @@ the distinct context K/V rows), and the same call launched back to back for
 ``long_decode`` times the decode step of the long-context workload (512
 sequences, contexts U[4096, 32768], 32 Q / 8 KV heads, about 38.7 GB of K/V
 per call) against the HBM peak. ``decode_gqa8`` times decode with eight query
-heads per KV head (64 Q / 8 KV, 256 sequences of 100-2048 tokens), the shape
-that runs on the MFMA tile form. ``hbm_copy_ceiling`` is torch's own copy over
+heads per KV head (64 Q / 8 KV, 256 sequences of 100-2048 tokens), a shape
+that runs on the row-tile kernel. ``hbm_copy_ceiling`` is torch's own copy over
 2 GiB. ``trace_replay`` replays
 the 28-layer scheduler trace (256 requests) and reports decode GB/s, prefill
 TFLOP/s and kernel-only tokens/s from events around each layer's kernels. ``cpu_baseline`` times the
@@ -607,7 +607,7 @@ def long_decode(torch, dev, steps: int, warmup: int) -> dict:
 def decode_gqa8(torch, dev, reps: int = 30) -> dict:
     """Decode with eight query heads per KV head (64 Q / 8 KV), 256 sequences of U[100, 2048] tokens on a
     shuffled pool: paged_attn_decode back to back (HIP events around `reps` calls on the stream). This shape
-    runs on the MFMA tile form (one work-group per sequence and KV head)."""
+    runs on the row-tile kernel (eight wavefronts per CU, one per KV head, streaming 16-token tiles)."""
     from paged_kv_attention_28_amd import binding as B
     rng = np.random.default_rng(8)
     S, hq, hkv, d = 256, 64, 8, 128
@@ -648,7 +648,7 @@ def decode_gqa8(torch, dev, reps: int = 30) -> dict:
     return {"workload": "decode, 256 seqs, context U[100, 2048], GQA 64Q/8KV (eight query heads per KV head), "
                         "head_dim 128, bf16, block 256, shuffled pool; paged_attn_decode back to back",
             "us": round(us, 2), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": byts, "form": "MFMA tile form (one work-group per sequence and KV head)"}
+            "algorithmic_bytes": byts, "form": "row-tile kernel (stream-K over 16-token tiles, one wavefront per KV head)"}
 
 
 def graph_vs_eager(torch, dev, iters: int = 50, num_layers: int = 28):

@@ -180,12 +180,20 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * sequence, key chunk) with up to 16 chunks of at least 4 x 32 keys, whose
  * partials (at most about 6.5 MB) go to the workspace and are merged by a
  * second kernel in chunk order; the chunking depends only on num_seqs,
- * num_kv_heads and max_context_len. Two or four query heads per KV head take
- * the same tile kernel for small calls (num_seqs <= 4, or num_seqs <= 48 with
- * max_context_len <= 1024), the stream-K kernel otherwise; the environment
- * variable PKV_DECODE_FORM=tile or =rowwide, read on every call, forces one
- * of the two for two or four query heads per KV head (tests, tuning). The
- * two forms round differently (the tile form's weights are bf16), so their
+ * num_kv_heads and max_context_len. With eight KV heads, eight query heads
+ * per KV head take a third kernel on calls of num_seqs >= 64 with
+ * max_context_len > 1024, or num_seqs >= 8 with max_context_len > 4096 (and
+ * num_seqs <= 4000): stream-K over 16-token tiles, one work-group of eight
+ * wavefronts per CU (one per KV head), its partials (64 query heads x 1040
+ * bytes per work-group) merged by the stream-K kernel's merge; the split
+ * depends only on the context lengths, max_context_len and the CU count.
+ * Two or four query heads per KV head take the tile kernel for small calls
+ * (num_seqs <= 4, or num_seqs <= 48 with max_context_len <= 1024), the
+ * stream-K kernel otherwise. The environment variable PKV_DECODE_FORM=tile,
+ * =rowwide or =rowtile, read on every call, forces one of the forms that
+ * take the shape (tests, tuning): tile or rowwide for two or four query heads
+ * per KV head, tile or rowtile for eight (rowtile needs eight KV heads). The
+ * forms round differently (the tile forms' weights are bf16), so their
  * outputs differ within the attention tolerance, not bit for bit.
  */
 pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -216,7 +224,8 @@ pkv_status paged_attn_decode(void* out, const void* q, const void* k_cache, cons
  * slots, per resident wavefront, plus 4 bytes per sequence: 32 query heads
  * fit on 1024 resident wavefronts; eight query heads per KV head take the tile form
  * described under paged_attn_decode, whose partials need at most about
- * 6.5 MB) and PKV_ERR_HIP when the array's device address cannot be found.
+ * 6.5 MB, or the row-tile kernel, 64 x 1040 bytes per CU) and PKV_ERR_HIP
+ * when the array's device address cannot be found.
  */
 pkv_status paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
                                      const int32_t* block_tables, int32_t block_table_stride,

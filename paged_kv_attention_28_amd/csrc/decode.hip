@@ -70,6 +70,13 @@ constexpr int kMaxSeqs = 8192;     // LDS scan capacity
 constexpr int kTileFewSeqs = 4;
 constexpr int kTileShortSeqs = 48;
 constexpr int kTileShortCtx = 1024;
+// eight query heads per KV head: calls of at least kRowTileSeqs sequences with max_context_len above
+// kRowTileCtx, or of at least kRowTileLongSeqs with max_context_len above kRowTileLongCtx, take the row-tile
+// kernel; the rest the tile form
+constexpr int kRowTileSeqs = 64;
+constexpr int kRowTileCtx = 1024;
+constexpr int kRowTileLongSeqs = 8;
+constexpr int kRowTileLongCtx = 4096;
 // LDS reserved per stream work-group: more than half a CU's 160 KiB, so each
 // CU holds one work-group (one wavefront per SIMD). On the 256-sequence
 // decode workload this ran 6.5 % faster than two per CU: each wavefront walks
@@ -715,6 +722,391 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row-tile decode (eight query heads per KV head, eight KV heads: 64 Q /
+// 8 KV): stream-K over 16-token tiles, one work-group of eight wavefronts per
+// CU, wavefront g streaming KV head g.
+//
+// A tile is 16 consecutive tokens of one sequence (inside one cache block).
+// The global tile list (sequences in order) is divided evenly over the
+// work-groups; every wavefront of a work-group walks the work-group's tiles
+// for its own KV head, on its own (no barrier in the loop), with two tiles
+// in flight while it computes a third: head g's K rows go straight into
+// registers in the layout of the MFMA A operand, head g's V rows into a
+// three-stage ring in LDS private to the wavefront (direct-to-LDS loads),
+// from which the transposing LDS read forms V^T; the cache rows are read
+// with nontemporal loads. The first tile of each sequence also brings the
+// sequence's eight query rows of the head group into that stage's LDS slot,
+// read into registers once per sequence. S^T = K_g Q^T with
+// v_mfma_f32_16x16x32_bf16 (16 keys x 16 query rows, the G query heads of
+// the KV head padded to 16), an online softmax per query row across the four
+// lane groups that hold its 16 scores, and O^T += V_g^T P^T with
+// v_mfma_f32_16x16x16_bf16, whose B operand is the weights exactly as the
+// S^T accumulators hold them (lane l: keys 4 (l / 16) .. + 3 of query row
+// l % 16). Sequences cut between work-groups leave fp32 (m, l, o) partials
+// in the same layout as the row-wide kernel (work-group w, slot 0 for the
+// piece that starts its range, slot 1 for the one that ends it), so the same
+// merge kernels combine them, with tiles as the steps. V chunks are
+// XOR-swizzled in the ring (by 4 t % 16 for token t of the tile), which keeps
+// the transposing reads free of bank conflicts. Positions past the context
+// load its last row (always written) and are masked.
+// ---------------------------------------------------------------------------
+
+constexpr int kRT = 16;                             // tokens per row tile
+constexpr int kRTKv = 8;                            // KV heads (one wavefront each)
+constexpr int kRTRow = kRTKv * kHeadDim * 2;        // 2 KiB: one token's K (or V) row
+constexpr int kRTMinTiles = 2;                      // tiles per work-group at least
+constexpr int kRTMaxSeqs = 4000;                    // LDS scan capacity beside the rings and query slots
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+template <int N>
+struct RTStage {
+  static constexpr int value = N;
+};
+// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at their maxima; gfx9 encoding)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane
+// 4k + c names row k, 4-element chunk c; lane i receives element i of the
+// group's 4 x 16 block from rows 0..3.
+__device__ __forceinline__ uint2 rt_read_tr16(const char* __restrict__ p) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+#pragma clang diagnostic pop
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Work-group scan of per-sequence tile counts (NT threads): pre[b] = first
+// global tile of sequence b, pre[S] = total.
+template <int NT>
+__device__ void scan_units(int* pre, const int32_t* __restrict__ ctx, int S, int max_ctx, int unit) {
+  __shared__ int wsum[NT / 64];
+  const int tid = threadIdx.x;
+  const int per = (S + NT - 1) / NT;
+  const int lo = tid * per;
+  const int hi = lo + per < S ? lo + per : S;
+  int sum = 0;
+  for (int b = lo; b < hi; ++b) sum += (clamp_len(ctx[b], max_ctx) + unit - 1) / unit;
+  int x = sum;  // inclusive scan inside the wavefront
+  const int lane = tid & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[tid >> 6] = x;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
+  int run = base + x - sum;
+  for (int b = lo; b < hi; ++b) {
+    pre[b] = run;
+    run += (clamp_len(ctx[b], max_ctx) + unit - 1) / unit;
+  }
+  if (tid == NT - 1) pre[S] = base + x;
+  __syncthreads();
+}
+
+// One tile of the work-group's range: sequence, tile index inside it, first token, valid tokens, cache block.
+struct RowTile {
+  int b, st, tok0, nvalid;
+  int blk;    // cache block (checked against the pool)
+  int last;   // last tile of its sequence
+  int qload;  // the wavefront starts this sequence here: its query rows come with the tile
+};
+
+constexpr int kNtAux = 2;                           // buffer-load cache policy: nontemporal
+constexpr int kRTStages = 3;                        // per-wavefront ring: two tiles in flight, one computed
+constexpr int kRTVSlice = kRT * kHeadDim * 2;       // 4 KiB: one KV head's V rows of a tile
+constexpr int kRTRing = kRTStages * kRTVSlice;      // 12 KiB of LDS per wavefront
+// per-stage LDS slot for a wavefront's G query rows (256 B each), a whole number of 1 KiB load instructions
+__host__ __device__ constexpr int rt_qslot(int G) { return G * kHeadDim * 2 > 1024 ? G * kHeadDim * 2 : 1024; }
+__host__ __device__ constexpr int rt_lds_fixed(int G) { return kRTKv * (kRTRing + kRTStages * rt_qslot(G)); }
+
+template <int G, bool FUSED>
+__global__ __launch_bounds__(512) void decode_rowtile_kernel(
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const char* __restrict__ k_cache,
+    const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables, int bt_stride,
+    const int32_t* __restrict__ context_lens, int num_seqs, int64_t num_blocks, float scale_log2, int max_ctx,
+    int32_t* __restrict__ header, float* __restrict__ part_ml, float* __restrict__ part_o, const NewRows nr) {
+  constexpr int HQ = G * kRTKv;
+  constexpr int QS = rt_qslot(G);
+  // eight wavefront V rings, eight wavefronts' query slots (one per stage), then the tile prefix
+  extern __shared__ __attribute__((aligned(16))) char rt_lds[];
+  int* pre = reinterpret_cast<int*>(rt_lds + rt_lds_fixed(G));
+
+  scan_units<512>(pre, context_lens, num_seqs, max_ctx, kRT);
+  const int T = pre[num_seqs];
+  const int W = gridDim.x;
+  int P = (T + W - 1) / W;
+  P = P > kRTMinTiles ? P : kRTMinTiles;
+  if (blockIdx.x == 0) {  // tile prefix and tiles per work-group for the merge kernel
+    for (int i = threadIdx.x; i <= num_seqs; i += 512) header[1 + i] = pre[i];
+    if (threadIdx.x == 0) header[0] = P;
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  }
+  const int s0 = blockIdx.x * P;
+  if (s0 >= T) return;
+  const int s1 = s0 + P < T ? s0 + P : T;
+  const int n = s1 - s0;
+
+  const int lane = threadIdx.x & 63;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // KV head of this wavefront
+  const int col = lane & 15;   // query row of the MFMA tiles; key row of the K operand
+  const int grp = lane >> 4;   // lane group: keys 4 grp .. 4 grp + 3 of the S^T tile
+  const bool row_real = col < G;
+  const uint32_t nblk32 = num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)num_blocks;
+  char* ring = rt_lds + g * kRTRing;
+  char* qslots = rt_lds + kRTKv * kRTRing + g * (kRTStages * QS);
+
+  // sequence holding global tile s0: pre[lo] <= s0 < pre[lo + 1]
+  int lo_b = 0, hi_b = num_seqs;
+  while (hi_b - lo_b > 1) {
+    const int mid = (lo_b + hi_b) >> 1;
+    if (pre[mid] <= s0) lo_b = mid; else hi_b = mid;
+  }
+  // tile metadata is wave-uniform: the sequence index goes through readfirstlane so that its context length
+  // and block id are scalar loads (a vector load there would make the loop wait for every load in flight)
+  auto rfl = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  auto make_tile = [&](int b, int st) -> RowTile {
+    RowTile t;
+    t.b = rfl(b);
+    t.st = rfl(st);
+    t.tok0 = t.st * kRT;
+    const int L = clamp_len(context_lens[t.b], max_ctx);
+    t.nvalid = L - t.tok0 < kRT ? L - t.tok0 : kRT;
+    t.last = rfl(t.st + 1 == pre[t.b + 1] - pre[t.b] ? 1 : 0);
+    const uint32_t blk32 = (uint32_t)block_tables[(int64_t)t.b * bt_stride + (t.tok0 >> 8)];
+    t.blk = rfl(blk32 < nblk32 ? (int)blk32 : 0);  // caller error: stay inside the pool
+    t.nvalid = rfl(t.nvalid);
+    t.qload = t.st == 0 ? 1 : 0;
+    return t;
+  };
+  auto next_tile = [&](const RowTile& t) -> RowTile {
+    if (!t.last) return make_tile(t.b, t.st + 1);
+    int nb = t.b + 1;
+    while (nb < num_seqs && pre[nb + 1] == pre[nb]) ++nb;
+    return make_tile(nb < num_seqs ? nb : t.b, 0);  // past the last sequence only when the range ends there
+  };
+
+  // Loads of a tile into ring stage ST (the cache rows are read once: nontemporal loads, which streamed 7-9 %
+  // faster than plain ones): head g's V rows into LDS (buffer loads with the lds bit, four 1 KiB
+  // instructions; instruction j writes tokens 4 j .. 4 j + 3, lane l token 4 j + grp, LDS chunk col, which
+  // holds logical chunk col ^ (4 token % 16)), issued first, then head g's K rows into registers in the MFMA A
+  // layout (lane l: key col, dims 32 kk + 8 grp .. + 7). Tokens past the context load its last row; with the
+  // fused store, the sequence's new token (its last position) comes from the step's input row. Buffer loads
+  // (not global_load_lds) keep the compiler's vmcnt accounting exact: it treats an LDS-writing global
+  // instruction like a flat access and then waits for every load in flight.
+  u32x4 kreg[kRTStages][4];
+  auto issue = [&](auto stage_c, const RowTile& t) {
+    constexpr int ST = decltype(stage_c)::value;
+    const int64_t row0 = (int64_t)t.blk * kBlockSize + (t.tok0 & (kBlockSize - 1));
+    const bool from_input = FUSED && nr.k && t.last;
+    const int t_new = t.nvalid - 1;
+    char* vst = ring + ST * kRTVSlice;
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + row0 * kRTRow + g * (kHeadDim * 2)), (short)0,
+                                          kRT * kRTRow, 0x00020000);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+    if (!from_input) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tr = 4 * j + grp;
+        const int te = tr < t.nvalid ? tr : t_new;
+        const uint32_t off = (uint32_t)(te * kRTRow + 16 * (col ^ ((4 * tr) & 15)));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vst + 1024 * j), 16, off, 0, 0, kNtAux);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t vi = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(nr.v + (int64_t)t.b * nr.v_stride_b + g * (kHeadDim * 2)), (short)0, kHeadDim * 2, 0x00020000);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tr = 4 * j + grp;
+        const int te = tr < t.nvalid ? tr : t_new;
+        const uint32_t ch16 = (uint32_t)(16 * (col ^ ((4 * tr) & 15)));
+        if (te != t_new)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vst + 1024 * j), 16, (uint32_t)(te * kRTRow) + ch16,
+                                                   0, 0, kNtAux);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vi, (lds_void_t*)(vst + 1024 * j), 16, ch16, 0, 0, 0);
+      }
+    }
+#pragma clang diagnostic pop
+    const int te = col < t.nvalid ? col : t_new;
+    const char* kp = (from_input && te == t_new)
+                         ? nr.k + (int64_t)t.b * nr.k_stride_b + g * (kHeadDim * 2) + 16 * grp
+                         : k_cache + (row0 + te) * kRTRow + g * (kHeadDim * 2) + 16 * grp;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kreg[ST][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 64 * kk));
+    // the sequence's G query rows of this head group into the stage's query slot (lane l of instruction j:
+    // row 4 j + grp, 16-byte chunk col, LDS offset 256 row + 16 col)
+    if (t.qload) {
+      const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(q + ((int64_t)t.b * HQ + g * G) * kHeadDim), (short)0, G * kHeadDim * 2, 0x00020000);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wold-style-cast"
+#pragma unroll
+      for (int j = 0; j < QS / 1024; ++j)
+        if (4 * j + grp < G)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void_t*)(qslots + ST * QS + 1024 * j), 16,
+                                                   (uint32_t)((4 * j + grp) * (kHeadDim * 2) + 16 * col), 0, 0, 0);
+#pragma clang diagnostic pop
+    }
+  };
+
+  // queries of the tile's sequence for the MFMA B operand, from the query slot of stage ST: lane l holds
+  // row l % 16 (query head g G + l % 16 when l % 16 < G, else zeros), dims 32 kk + 8 grp .. + 7
+  u32x4 qreg[4];
+  auto read_q = [&](int st_slot) {
+    const char* qp = qslots + st_slot * QS + (row_real ? col : 0) * (kHeadDim * 2) + 16 * grp;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qreg[kk] = row_real ? *reinterpret_cast<const u32x4*>(qp + 64 * kk) : u32x4{0u, 0u, 0u, 0u};
+  };
+
+  f32x4 acc[8];
+  float m_run, l_part;
+  auto reset = [&]() {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = kNegBig;
+    l_part = 0.f;
+  };
+  reset();
+  int piece_first = s0;
+
+  auto finish_piece = [&](const RowTile& t, int gidx) {
+    float l_row = l_part + __shfl_xor(l_part, 16);
+    l_row += __shfl_xor(l_row, 32);
+    const int pb = pre[t.b];
+    const int nb = pre[t.b + 1] - pb;
+    const bool whole = (pb / P) == ((pb + nb - 1) / P);
+    if (row_real) {
+      const int head = g * G + col;
+      if (whole) {
+        const float inv = 1.f / l_row;
+        uint16_t* op = out + ((int64_t)t.b * HQ + head) * kHeadDim + 4 * grp;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *reinterpret_cast<u32x2*>(op + 16 * db) =
+              u32x2{pack_bf16x2(acc[db][0] * inv, acc[db][1] * inv), pack_bf16x2(acc[db][2] * inv, acc[db][3] * inv)};
+      } else {
+        const int slot = piece_first == s0 ? 0 : 1;
+        const int64_t pidx = ((int64_t)blockIdx.x * 2 + slot) * HQ + head;
+        float* po = part_o + pidx * kHeadDim + 4 * grp;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(po + 16 * db) = acc[db];
+        if (grp == 0) {
+          part_ml[pidx * 2 + 0] = m_run;
+          part_ml[pidx * 2 + 1] = l_row;
+        }
+      }
+    }
+    reset();
+    piece_first = gidx + 1;
+  };
+
+  auto compute = [&](auto stage_c, const RowTile& t, int gi) {
+    constexpr int ST = decltype(stage_c)::value;
+    const char* vst = ring + ST * kRTVSlice;
+    if (t.qload) read_q(ST);
+    // S^T = K_g Q^T (16 keys x 16 query rows)
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[ST][kk]),
+                                                  __builtin_bit_cast(bf16x8, qreg[kk]), s, 0, 0, 0);
+    // lane l holds keys 4 grp + i (i = 0..3) of query row col; keys past the context are masked
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = 4 * grp + i < t.nvalid ? s[i] * scale_log2 : -__builtin_inff();
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+    const uint32_t w0 = pack_bf16x2(p[0], p[1]);
+    const uint32_t w1 = pack_bf16x2(p[2], p[3]);
+    // row sum of the weights as rounded to bf16 for the P V products
+    l_part = l_part * alpha + ((bf_lo(w0) + bf_hi(w0)) + (bf_lo(w1) + bf_hi(w1)));
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+    // O^T += V_g^T P^T: A = V^T (lane l: dim 16 db + l % 16 of keys 4 grp .. + 3) through the transposing
+    // read; lane 4 k + c of a group names key 4 grp + k, dims 16 db + 4 c .. + 3
+    const int vk = 4 * grp + ((lane & 15) >> 2);
+    const int vc = lane & 3;
+    const char* vrow = vst + vk * (kHeadDim * 2) + 8 * (vc & 1);
+    const bf16x4 pb4 = __builtin_bit_cast(bf16x4, u32x2{w0, w1});
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint2 va = rt_read_tr16(vrow + 16 * ((2 * db + (vc >> 1)) ^ ((4 * vk) & 15)));
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, va), pb4, acc[db], 0, 0, 0);
+    }
+    // fused store: head g's K (from registers) and V (from the ring) of the sequence's new token go to its slot
+    if constexpr (FUSED) {
+      if (nr.k && t.last) {
+        const int32_t slot = nr.slots[t.b];
+        const int tn = t.nvalid - 1;
+        if (slot >= 0 && (int64_t)slot < nr.num_slots) {
+          const int64_t dst = (int64_t)slot * kRTRow + g * (kHeadDim * 2);
+          if (col == tn) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+              *reinterpret_cast<u32x4*>(nr.k_cache + dst + 64 * kk + 16 * grp) = kreg[ST][kk];
+          }
+          if (grp == 0)
+            *reinterpret_cast<u32x4*>(nr.v_cache + dst + 16 * col) =
+                *reinterpret_cast<const u32x4*>(vst + tn * (kHeadDim * 2) + 16 * (col ^ ((4 * tn) & 15)));
+        }
+      }
+    }
+    if (t.last || gi + 1 == s1) {
+      finish_piece(t, gi);
+      // vmcnt also counts stores, and loads and stores may complete out of order: wait here for the piece's
+      // stores (and the tiles in flight), so that the loop's waits can count the loads alone
+      __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    }
+  };
+
+  // i-th tile of the range in ring stage ST: issue the tile two ahead into the stage freed by tile i - 1
+  // (past the range end the last tile again, so every iteration issues the same eight loads), wait until
+  // tile i's loads have landed (vmcnt counts this wavefront's memory operations in order: the sixteen loads of
+  // the two tiles after it may still be in flight), then compute it
+  RowTile tl[kRTStages];
+  auto iteration = [&](auto stage_c, int i) {
+    constexpr int ST = decltype(stage_c)::value;
+    constexpr int NX = (ST + 2) % kRTStages;
+    const RowTile& prev = tl[(ST + 1) % kRTStages];
+    tl[NX] = i + 2 < n ? next_tile(prev) : prev;
+    issue(RTStage<NX>{}, tl[NX]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(16));
+    __builtin_amdgcn_sched_barrier(0);
+    if (i < n) compute(stage_c, tl[ST], s0 + i);
+  };
+
+  tl[0] = make_tile(lo_b, s0 - pre[lo_b]);
+  tl[0].qload = 1;
+  issue(RTStage<0>{}, tl[0]);
+  tl[1] = n > 1 ? next_tile(tl[0]) : tl[0];
+  issue(RTStage<1>{}, tl[1]);
+  for (int i = 0; i < n; i += kRTStages) {
+    iteration(RTStage<0>{}, i);
+    iteration(RTStage<1>{}, i + 1);
+    iteration(RTStage<2>{}, i + 2);
+  }
+}
+
 struct Layout {
   size_t header_bytes, ml_bytes, o_bytes;  // header = steps per wavefront + step prefix
 };
@@ -784,7 +1176,7 @@ size_t stream_lds(int num_seqs) {
 
 // Resident work-groups of a decode kernel on the current device (cached per
 // device, kernel and LDS size), capped so the partial slots suffice; 0 on error.
-int resident_wgs(const void* kernel, size_t lds) {
+int resident_wgs(const void* kernel, size_t lds, int threads = 256) {
   static std::mutex mu;
   static struct Entry {
     int dev;
@@ -800,19 +1192,45 @@ int resident_wgs(const void* kernel, size_t lds) {
     if (cache[i].dev == dev && cache[i].k == kernel && cache[i].lds == lds) return cache[i].n;
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, lds) != hipSuccess || per < 1) per = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, lds) != hipSuccess || per < 1) per = 1;
   int n = cus * per;
-  if (n * 4 > kWavesCap) n = kWavesCap / 4;
+  if (n * 4 > kWavesCap) n = kWavesCap / 4;  // partial slots are sized for kWavesCap wavefronts (or work-groups)
   if (ncache < 128) cache[ncache++] = Entry{dev, kernel, lds, n};
   return n;
 }
+
+
+template <int G, bool FUSED>
+const void* rowtile_kernel() {
+  return reinterpret_cast<const void*>(&decode_rowtile_kernel<G, FUSED>);
+}
+
+size_t rowtile_lds(int G, int num_seqs) { return (size_t)rt_lds_fixed(G) + (size_t)(num_seqs + 1) * 4; }
+
+// Resident work-groups of the row-tile kernel (one per CU: its V rings and query slots take 144 KiB).
+int rowtile_grid(int G, int num_seqs) { return resident_wgs(rowtile_kernel<8, false>(), rowtile_lds(G, num_seqs), 512); }
+
+// Whether the row-tile kernel takes a call with these heads and sequences (eight query heads per KV head,
+// eight KV heads; its LDS scan holds up to kRTMaxSeqs sequences).
+bool rowtile_fits(int G, int num_kv_heads, int num_seqs) {
+  return num_kv_heads == kRTKv && G == 8 && num_seqs <= kRTMaxSeqs;
+}
+
+// The row-tile decode (decode_rowtile_kernel) and the merge of its partials. `wsb` is the workspace laid out
+// as `lo` for `grid` work-groups (two partial slots each).
+pkv_status rowtile_call(uint16_t* o, const uint16_t* qq, const char* kc, const char* vc, const int32_t* block_tables,
+                        int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs, int G,
+                        int64_t num_blocks, float scale_log2, int32_t max_context_len, int grid, char* wsb,
+                        const Layout& lo, hipStream_t s, const NewRows& nr);
 
 }  // namespace
 
 bool decode_prepare(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_seqs) {
   if (num_kv_heads < 1 || num_q_heads < num_kv_heads || num_q_heads % num_kv_heads || num_seqs < 1) return false;
-  if (num_q_heads / num_kv_heads == 8) return true;  // the tile form queries nothing
-  return resident_wgs(pick_kernel(num_q_heads / num_kv_heads, num_kv_heads), stream_lds(num_seqs)) > 0;
+  const int G = num_q_heads / num_kv_heads;
+  if (rowtile_fits(G, num_kv_heads, num_seqs) && rowtile_grid(G, num_seqs) <= 0) return false;
+  if (G == 8) return true;  // the tile form queries nothing
+  return resident_wgs(pick_kernel(G, num_kv_heads), stream_lds(num_seqs)) > 0;
 }
 
 }  // namespace pkv
@@ -882,12 +1300,47 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   // us. 16 Q / 8 KV, a 28-layer decode step with the store fused, each layer its own caches: contexts of
   // 100-1024 tokens, 16-48 sequences 5-10 % faster on the tile form, 64 sequences 6 % slower; contexts of
   // 1024-2048 tokens, 8-64 sequences 5-17 % slower; 1-4 sequences of any length level or faster.
-  // PKV_DECODE_FORM=tile or =rowwide in the environment overrides the choice for two or four query heads
-  // per KV head (read on every call; for tests and tuning)
+  // With eight query heads per KV head and eight KV heads, calls that stream longer contexts over enough
+  // sequences take the row-tile kernel (decode_rowtile_kernel): a 28-layer decode step with the store fused,
+  // each layer its own caches, 64 Q / 8 KV, tile form -> row-tile kernel: contexts of 100-2048 tokens, 64-256
+  // sequences 6-12 % faster, 32 or fewer 6-28 % slower; 1024-8192 tokens, 8-64 sequences 8-20 % faster;
+  // contexts of 100-1024 tokens level or slower at every batch size.
+  // PKV_DECODE_FORM=tile, =rowwide or =rowtile in the environment overrides the choice (read on every call;
+  // for tests and tuning; eight query heads per KV head never take the row-wide kernel, and the row-tile
+  // kernel needs eight KV heads)
   const char* form = getenv("PKV_DECODE_FORM");
   const bool force_tile = form && !strcmp(form, "tile");
   const bool force_rowwide = form && !strcmp(form, "rowwide");
+  const bool force_rowtile = form && !strcmp(form, "rowtile");
   const bool small_call = num_seqs <= kTileFewSeqs || (num_seqs <= kTileShortSeqs && max_context_len <= kTileShortCtx);
+  // the row-tile kernel counts 16-token tiles in 32-bit integers
+  const bool rowtile_ok = rowtile_fits(G, num_kv_heads, num_seqs) &&
+                          (int64_t)num_seqs * ((max_context_len + kRT - 1) / kRT) <= INT32_MAX;
+  const bool rowtile_pick = G == 8 && ((num_seqs >= kRowTileSeqs && max_context_len > kRowTileCtx) ||
+                                       (num_seqs >= kRowTileLongSeqs && max_context_len > kRowTileLongCtx));
+  if (rowtile_ok && (force_rowtile || (rowtile_pick && !force_tile))) {
+    const int grid = rowtile_grid(G, num_seqs);
+    if (grid <= 0) return fail(PKV_ERR_HIP, "paged_attn_decode: cannot query the device");
+    Layout lo;
+    char* wsb;
+    if (use_scratch) {
+      lo = workspace_layout(num_seqs, num_q_heads, grid);
+      const size_t need = lo.header_bytes + lo.ml_bytes + lo.o_bytes;
+      if (need > kScratchBytes)
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "paged_attn_decode_noalloc: %d query heads on %d work-groups need %zu bytes of workspace, more "
+                    "than the library's %zu-byte scratch", num_q_heads, grid, need, kScratchBytes);
+      wsb = scratch_address();
+      if (!wsb) return fail(PKV_ERR_HIP, "paged_attn_decode_noalloc: cannot find the device's scratch array");
+    } else {
+      lo = workspace_layout(num_seqs, num_q_heads);
+      wsb = static_cast<char*>(workspace);
+    }
+    return rowtile_call(static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+                        static_cast<const char*>(k_cache), static_cast<const char*>(v_cache), block_tables,
+                        block_table_stride, context_lens, num_seqs, G, num_blocks, scale * 1.4426950408889634f,
+                        max_context_len, grid, wsb, lo, reinterpret_cast<hipStream_t>(stream), nr);
+  }
   if (G == 8 || (G >= 2 && !force_rowwide && (force_tile || small_call))) {
     void* tws = workspace;
     size_t tws_bytes = workspace_bytes;
@@ -979,6 +1432,35 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
     default: return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: %d query heads", num_q_heads);
   }
   return check_launch("paged_attn_decode (merge)");
+}
+
+pkv_status rowtile_call(uint16_t* o, const uint16_t* qq, const char* kc, const char* vc, const int32_t* block_tables,
+                        int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs, int G,
+                        int64_t num_blocks, float scale_log2, int32_t max_context_len, int grid, char* wsb,
+                        const Layout& lo, hipStream_t s, const NewRows& nr) {
+  int32_t* header = reinterpret_cast<int32_t*>(wsb);
+  float* part_ml = reinterpret_cast<float*>(wsb + lo.header_bytes);
+  float* part_o = reinterpret_cast<float*>(wsb + lo.header_bytes + lo.ml_bytes);
+  const size_t lds = rowtile_lds(G, num_seqs);
+#define PKV_RT_LAUNCH(GG, FF)                                                                                  \
+  hipLaunchKernelGGL((decode_rowtile_kernel<GG, FF>), dim3(grid), dim3(512), lds, s, o, qq, kc, vc, block_tables, \
+                     block_table_stride, context_lens, num_seqs, num_blocks, scale_log2, max_context_len, header, \
+                     part_ml, part_o, nr)
+  if (nr.k)
+    PKV_RT_LAUNCH(8, true);
+  else
+    PKV_RT_LAUNCH(8, false);
+#undef PKV_RT_LAUNCH
+  pkv_status st = check_launch("paged_attn_decode (row tiles)");
+  if (st != PKV_OK) return st;
+  // 64 query heads (G = 8 on eight KV heads)
+  if (num_seqs <= kWideMergeMaxSeqs)
+    hipLaunchKernelGGL((decode_merge_wide_kernel<64>), dim3(num_seqs, 64), dim3(1024), 0, s, o, header, part_ml,
+                       part_o, context_lens);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(num_seqs), dim3(64 * 16), 0, s, o, header, part_ml, part_o,
+                       context_lens);
+  return check_launch("paged_attn_decode (row-tile merge)");
 }
 
 }  // namespace

@@ -267,6 +267,12 @@ EDGE = {
     "decode_tile_split_one_long": _dec([40000], hq=64),
     "decode_tile_split_few": _dec([9000, 300, 1, 12000], hq=64, **PEAKY),
     "decode_tile_split_hkv1": _dec([5, 2500, 777], hq=8, hkv=1),
+    # eight query heads on eight KV heads, the row-tile kernel's edges: contexts on both sides of its 16-token
+    # tiles and of a cache block, sequence ends inside every work-group's range, padding rows, more than 32
+    # sequences (serial merge); the most sequences its LDS scan holds (4000)
+    "decode_rowtile_ragged": _dec([1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 3000, 1025]
+                                  + [(89 * i) % 2200 + 1 for i in range(88)], hq=64, pad=2),
+    "decode_rowtile_4000seqs": _dec([(13 * i) % 40 + 1 for i in range(4000)], hq=64),
     # more than 32 sequences with 8 and 4 query heads: the per-sequence (serial) merge
     "decode_hq8_hkv4_40seqs": _dec([(41 * i) % 900 + 1 for i in range(40)], hq=8, hkv=4),
     "decode_hq4_hkv1_40seqs": _dec([(29 * i) % 1300 + 1 for i in range(40)], hq=4, hkv=1),
@@ -357,15 +363,20 @@ def _g(case: dict) -> int:
     return case.get("hq", 16) // case.get("hkv", 8)
 
 
-# decode cases with two or four query heads per KV head, which either decode form can take
+# decode cases with two or four query heads per KV head, which the row-wide kernel and the tile form take
 DECODE_FORM_CASES = sorted(n for n, c in EDGE.items() if c.get("kind") == "decode" and _g(c) in (2, 4))
+# decode cases with eight query heads on eight KV heads, which the tile form and the row-tile kernel take
+ROWTILE_CASES = sorted(n for n, c in EDGE.items()
+                       if c.get("kind") == "decode" and _g(c) == 8 and c.get("hkv", 8) == 8)
+FORM_PARAMS = ([(n, f) for n in DECODE_FORM_CASES for f in ("rowwide", "tile")]
+               + [(n, f) for n in ROWTILE_CASES for f in ("tile", "rowtile")])
 
 
-@pytest.mark.parametrize("form", ["rowwide", "tile"])
-@pytest.mark.parametrize("name", DECODE_FORM_CASES)
+@pytest.mark.parametrize("name,form", FORM_PARAMS)
 def test_decode_forms_parity(name, form, monkeypatch):
-    """Every decode edge case with two or four query heads per KV head in both decode forms (the row-wide
-    stream-K kernel and the MFMA tile form, forced with PKV_DECODE_FORM) against the oracle."""
+    """Every decode edge case in each decode form that takes its shape (forced with PKV_DECODE_FORM): the
+    row-wide stream-K kernel and the MFMA tile form for two or four query heads per KV head, the tile form and
+    the row-tile kernel for eight on eight KV heads, against the oracle."""
     monkeypatch.setenv("PKV_DECODE_FORM", form)
     w = custom(**EDGE[name])
     dw = H.DeviceWorkload(w).build()
@@ -386,17 +397,26 @@ def _boundary(n, hi, hq, seed):
     return _dec(lens, hq=hq, hkv=8, seed=seed)
 
 
-# calls on both sides of the rule that sends two or four query heads per KV head to the tile form (at most 4
-# sequences, or at most 48 with max_context_len <= 1024): name -> (case, form the default dispatch must take)
+# calls on both sides of the rules that pick the decode form: two or four query heads per KV head take the tile
+# form for at most 4 sequences, or at most 48 with max_context_len <= 1024 (else the row-wide kernel); eight on
+# eight KV heads take the row-tile kernel for at least 64 sequences with max_context_len > 1024, or at least 8
+# with max_context_len > 4096 (else the tile form): name -> (case, form the default dispatch must take, the
+# other form of the shape)
 DISPATCH_CASES = {
-    "g2_4seqs_2048": (_boundary(4, 2048, 16, 41), "tile"),
-    "g2_5seqs_2048": (_boundary(5, 2048, 16, 42), "rowwide"),
-    "g2_48seqs_1024": (_boundary(48, 1024, 16, 43), "tile"),
-    "g2_49seqs_1024": (_boundary(49, 1024, 16, 44), "rowwide"),
-    "g2_48seqs_1025": (_boundary(48, 1025, 16, 45), "rowwide"),
-    "g4_4seqs_4096": (_boundary(4, 4096, 32, 46), "tile"),
-    "g4_48seqs_1024": (_boundary(48, 1024, 32, 47), "tile"),
-    "g4_49seqs_1024": (_boundary(49, 1024, 32, 48), "rowwide"),
+    "g2_4seqs_2048": (_boundary(4, 2048, 16, 41), "tile", "rowwide"),
+    "g2_5seqs_2048": (_boundary(5, 2048, 16, 42), "rowwide", "tile"),
+    "g2_48seqs_1024": (_boundary(48, 1024, 16, 43), "tile", "rowwide"),
+    "g2_49seqs_1024": (_boundary(49, 1024, 16, 44), "rowwide", "tile"),
+    "g2_48seqs_1025": (_boundary(48, 1025, 16, 45), "rowwide", "tile"),
+    "g4_4seqs_4096": (_boundary(4, 4096, 32, 46), "tile", "rowwide"),
+    "g4_48seqs_1024": (_boundary(48, 1024, 32, 47), "tile", "rowwide"),
+    "g4_49seqs_1024": (_boundary(49, 1024, 32, 48), "rowwide", "tile"),
+    "g8_64seqs_1025": (_boundary(64, 1025, 64, 51), "rowtile", "tile"),
+    "g8_63seqs_2048": (_boundary(63, 2048, 64, 52), "tile", "rowtile"),
+    "g8_64seqs_1024": (_boundary(64, 1024, 64, 53), "tile", "rowtile"),
+    "g8_8seqs_4097": (_boundary(8, 4097, 64, 54), "rowtile", "tile"),
+    "g8_7seqs_4097": (_boundary(7, 4097, 64, 55), "tile", "rowtile"),
+    "g8_8seqs_4096": (_boundary(8, 4096, 64, 56), "tile", "rowtile"),
 }
 
 
@@ -404,18 +424,17 @@ DISPATCH_CASES = {
 def test_decode_dispatch_boundaries(name, monkeypatch):
     """At each boundary of the decode form rule the default call gives exactly the bits of the form the rule
     names (the two forms round differently, so their bits tell them apart), and matches the oracle."""
-    case, expect = DISPATCH_CASES[name]
+    case, expect, other = DISPATCH_CASES[name]
     w = custom(**case)
     dw = H.DeviceWorkload(w).build()
     kc, vc = O.build_caches(w, device="cuda")
     p = w.passes[0]
     q, m = dw.pass_inputs(p)
     outs = {}
-    for form in ("auto", "tile", "rowwide"):
+    for form in ("auto", expect, other):
         monkeypatch.setenv("PKV_DECODE_FORM", form)
         outs[form] = dw.run_pass(p, q, m).clone()
     monkeypatch.delenv("PKV_DECODE_FORM")
-    other = "rowwide" if expect == "tile" else "tile"
     assert torch.equal(outs["auto"].view(torch.int16), outs[expect].view(torch.int16)), f"{name}: not the {expect} form"
     assert not torch.equal(outs[expect].view(torch.int16), outs[other].view(torch.int16)), f"{name}: forms agree bit for bit"
     ref = O.run_pass(w, p, kc, vc, q=q)
@@ -426,11 +445,14 @@ def test_decode_dispatch_boundaries(name, monkeypatch):
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
                "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
                "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs", "decode_tile_gqa8_pad",
-               "decode_tile_gqa8_long", "decode_tile_split_few", "decode_tile_split_hkv1"]
+               "decode_tile_gqa8_long", "decode_tile_split_few", "decode_tile_split_hkv1", "decode_rowtile_ragged"]
 
 
-@pytest.mark.parametrize("form", ["auto", "rowwide"])
-@pytest.mark.parametrize("case", FUSED_CASES)
+FUSED_PARAMS = ([(c, f) for c in FUSED_CASES for f in ("auto", "rowwide")]
+                + [(c, "rowtile") for c in FUSED_CASES if c in ROWTILE_CASES])
+
+
+@pytest.mark.parametrize("case,form", FUSED_PARAMS)
 def test_decode_store_fused_matches_two_calls(case, form, monkeypatch):
     """paged_attn_decode_store (new token read from its input row and stored by the wavefront that
     reads it) gives the bits of kv_store followed by paged_attn_decode: outputs and both caches."""

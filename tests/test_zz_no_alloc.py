@@ -2,9 +2,9 @@
 array, for callers that cannot allocate) against paged_attn_decode with a
 caller workspace: identical bits on two calls in a row, the second with a
 smaller batch (the scratch then still holds the first call's partials), and
-the oracle on both; with 64 query heads (eight per KV head) both calls run
-on the MFMA tile form, the second one split over the keys with its partials
-in the scratch. (A launch needing more than the scratch is rejected on the
+the oracle on both; with 64 query heads (eight per KV head) the first call
+runs on the row-tile kernel (its partials in the scratch) and the second on
+the MFMA tile form, split over the keys with its partials in the scratch. (A launch needing more than the scratch is rejected on the
 host; on a 256-CU GPU no supported shape does: the row-wide kernel needs at
 most about 34 MB with 32 query heads, the tile form's partials about 6.5 MB.)"""
 
