@@ -188,7 +188,9 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * bytes per work-group) merged by the stream-K kernel's merge; the split
  * depends only on the context lengths, max_context_len and the CU count.
  * Two or four query heads per KV head take the tile kernel for small calls
- * (num_seqs <= 4, or num_seqs <= 48 with max_context_len <= 1024), the
+ * (num_seqs <= 4; num_seqs <= 48 with two or 80 with four query heads per
+ * KV head and max_context_len <= 1024; with four also num_seqs <= 32 and
+ * max_context_len <= 2048), the
  * stream-K kernel otherwise. The environment variable PKV_DECODE_FORM=tile,
  * =rowwide or =rowtile, read on every call, forces one of the forms that
  * take the shape (tests, tuning): tile or rowwide for two or four query heads

@@ -66,10 +66,15 @@ constexpr int kMinStepsPerWave = 4;
 constexpr int kWideMergeMaxSeqs = 32;  // batches up to this size merge per (sequence, head)
 constexpr int kMaxSeqs = 8192;     // LDS scan capacity
 // two or four query heads per KV head: calls of up to kTileFewSeqs sequences, or of up to kTileShortSeqs
-// sequences with max_context_len up to kTileShortCtx, take the tile form
+// (two query heads per KV head) or kTileShortSeqsG4 (four) sequences with max_context_len up to
+// kTileShortCtx, take the tile form; with four, also calls of up to kTileMidSeqsG4 sequences with
+// max_context_len up to kTileMidCtx
 constexpr int kTileFewSeqs = 4;
 constexpr int kTileShortSeqs = 48;
+constexpr int kTileShortSeqsG4 = 80;
 constexpr int kTileShortCtx = 1024;
+constexpr int kTileMidSeqsG4 = 32;
+constexpr int kTileMidCtx = 2048;
 // eight query heads per KV head: calls of at least kRowTileSeqs sequences with max_context_len above
 // kRowTileCtx, or of at least kRowTileLongSeqs with max_context_len above kRowTileLongCtx, take the row-tile
 // kernel; the rest the tile form
@@ -1299,7 +1304,10 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   // 16: 45.8 -> 20.7, 256: 282.5 -> 223.5 us; 4096-32768 tokens, 1 sequence 56.1 -> 45.8 us, 128: 2197 -> 1754
   // us. 16 Q / 8 KV, a 28-layer decode step with the store fused, each layer its own caches: contexts of
   // 100-1024 tokens, 16-48 sequences 5-10 % faster on the tile form, 64 sequences 6 % slower; contexts of
-  // 1024-2048 tokens, 8-64 sequences 5-17 % slower; 1-4 sequences of any length level or faster.
+  // 1024-2048 tokens, 8-64 sequences 5-17 % slower; 1-4 sequences of any length level or faster. 32 Q / 8 KV,
+  // the same step: 100-1024 tokens, 48-80 sequences 1-17 % faster on the tile form, 96 and 128 9-14 % slower;
+  // 100-2048 tokens, 8-32 sequences 1-12 % faster, 48 and 64 4-13 % slower; 100-4096 tokens, 8-32 sequences
+  // 5-13 % slower.
   // With eight query heads per KV head and eight KV heads, calls that stream longer contexts over enough
   // sequences take the row-tile kernel (decode_rowtile_kernel): a 28-layer decode step with the store fused,
   // each layer its own caches, 64 Q / 8 KV, tile form -> row-tile kernel: contexts of 100-2048 tokens, 64-256
@@ -1312,7 +1320,10 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   const bool force_tile = form && !strcmp(form, "tile");
   const bool force_rowwide = form && !strcmp(form, "rowwide");
   const bool force_rowtile = form && !strcmp(form, "rowtile");
-  const bool small_call = num_seqs <= kTileFewSeqs || (num_seqs <= kTileShortSeqs && max_context_len <= kTileShortCtx);
+  const bool small_call =
+      num_seqs <= kTileFewSeqs ||
+      (num_seqs <= (G == 4 ? kTileShortSeqsG4 : kTileShortSeqs) && max_context_len <= kTileShortCtx) ||
+      (G == 4 && num_seqs <= kTileMidSeqsG4 && max_context_len <= kTileMidCtx);
   // the row-tile kernel counts 16-token tiles in 32-bit integers
   const bool rowtile_ok = rowtile_fits(G, num_kv_heads, num_seqs) &&
                           (int64_t)num_seqs * ((max_context_len + kRT - 1) / kRT) <= INT32_MAX;

@@ -398,7 +398,8 @@ def _boundary(n, hi, hq, seed):
 
 
 # calls on both sides of the rules that pick the decode form: two or four query heads per KV head take the tile
-# form for at most 4 sequences, or at most 48 with max_context_len <= 1024 (else the row-wide kernel); eight on
+# form for at most 4 sequences, or at most 48 (two) or 80 (four) with max_context_len <= 1024, and four also for
+# at most 32 with max_context_len <= 2048 (else the row-wide kernel); eight on
 # eight KV heads take the row-tile kernel for at least 64 sequences with max_context_len > 1024, or at least 8
 # with max_context_len > 4096 (else the tile form): name -> (case, form the default dispatch must take, the
 # other form of the shape)
@@ -409,8 +410,12 @@ DISPATCH_CASES = {
     "g2_49seqs_1024": (_boundary(49, 1024, 16, 44), "rowwide", "tile"),
     "g2_48seqs_1025": (_boundary(48, 1025, 16, 45), "rowwide", "tile"),
     "g4_4seqs_4096": (_boundary(4, 4096, 32, 46), "tile", "rowwide"),
-    "g4_48seqs_1024": (_boundary(48, 1024, 32, 47), "tile", "rowwide"),
-    "g4_49seqs_1024": (_boundary(49, 1024, 32, 48), "rowwide", "tile"),
+    "g4_5seqs_4096": (_boundary(5, 4096, 32, 57), "rowwide", "tile"),
+    "g4_80seqs_1024": (_boundary(80, 1024, 32, 47), "tile", "rowwide"),
+    "g4_81seqs_1024": (_boundary(81, 1024, 32, 48), "rowwide", "tile"),
+    "g4_32seqs_2048": (_boundary(32, 2048, 32, 58), "tile", "rowwide"),
+    "g4_33seqs_2048": (_boundary(33, 2048, 32, 59), "rowwide", "tile"),
+    "g4_32seqs_2049": (_boundary(32, 2049, 32, 60), "rowwide", "tile"),
     "g8_64seqs_1025": (_boundary(64, 1025, 64, 51), "rowtile", "tile"),
     "g8_63seqs_2048": (_boundary(63, 2048, 64, 52), "tile", "rowtile"),
     "g8_64seqs_1024": (_boundary(64, 1024, 64, 53), "tile", "rowtile"),
