@@ -736,13 +736,14 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 // The global tile list (sequences in order) is divided evenly over the
 // work-groups; every wavefront of a work-group walks the work-group's tiles
 // for its own KV head, on its own (no barrier in the loop), with two tiles
-// in flight while it computes a third: head g's K rows go straight into
-// registers in the layout of the MFMA A operand, head g's V rows into a
-// three-stage ring in LDS private to the wavefront (direct-to-LDS loads),
-// from which the transposing LDS read forms V^T; the cache rows are read
-// with nontemporal loads. The first tile of each sequence also brings the
-// sequence's eight query rows of the head group into that stage's LDS slot,
-// read into registers once per sequence. S^T = K_g Q^T with
+// in flight while it computes a third: head g's K and V rows of a tile come
+// into registers with nontemporal loads, each 16-lane group reading one
+// whole 256-byte row, and the computing tile's rows are written to LDS
+// private to the wavefront, from which K is read back in the layout of the
+// MFMA A operand and the transposing LDS read forms V^T. The first tile of
+// each sequence also brings the sequence's eight query rows of the head
+// group into that stage's LDS slot (direct-to-LDS buffer loads), read into
+// registers once per sequence. S^T = K_g Q^T with
 // v_mfma_f32_16x16x32_bf16 (16 keys x 16 query rows, the G query heads of
 // the KV head padded to 16), an online softmax per query row across the four
 // lane groups that hold its 16 scores, and O^T += V_g^T P^T with
@@ -751,9 +752,9 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 // l % 16). Sequences cut between work-groups leave fp32 (m, l, o) partials
 // in the same layout as the row-wide kernel (work-group w, slot 0 for the
 // piece that starts its range, slot 1 for the one that ends it), so the same
-// merge kernels combine them, with tiles as the steps. V chunks are
-// XOR-swizzled in the ring (by 4 t % 16 for token t of the tile), which keeps
-// the transposing reads free of bank conflicts. Positions past the context
+// merge kernels combine them, with tiles as the steps. The 16-byte chunks of
+// row t are XOR-swizzled in LDS (by t % 16 for K, 4 t % 16 for V), which
+// keeps the operand reads free of bank conflicts. Positions past the context
 // load its last row (always written) and are masked.
 // ---------------------------------------------------------------------------
 
@@ -761,7 +762,7 @@ constexpr int kRT = 16;                             // tokens per row tile
 constexpr int kRTKv = 8;                            // KV heads (one wavefront each)
 constexpr int kRTRow = kRTKv * kHeadDim * 2;        // 2 KiB: one token's K (or V) row
 constexpr int kRTMinTiles = 2;                      // tiles per work-group at least
-constexpr int kRTMaxSeqs = 4000;                    // LDS scan capacity beside the rings and query slots
+constexpr int kRTMaxSeqs = 4000;                    // LDS scan capacity beside the tile rows and query slots
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 template <int N>
@@ -823,10 +824,9 @@ struct RowTile {
   int qload;  // the wavefront starts this sequence here: its query rows come with the tile
 };
 
-constexpr int kNtAux = 2;                           // buffer-load cache policy: nontemporal
-constexpr int kRTStages = 3;                        // per-wavefront ring: two tiles in flight, one computed
-constexpr int kRTVSlice = kRT * kHeadDim * 2;       // 4 KiB: one KV head's V rows of a tile
-constexpr int kRTRing = kRTStages * kRTVSlice;      // 12 KiB of LDS per wavefront
+constexpr int kRTStages = 3;                        // per wavefront: two tiles in flight, one computed
+constexpr int kRTVSlice = kRT * kHeadDim * 2;       // 4 KiB: one KV head's K (or V) rows of a tile
+constexpr int kRTRing = 2 * kRTVSlice;              // 8 KiB of LDS per wavefront: the computed tile's K and V
 // per-stage LDS slot for a wavefront's G query rows (256 B each), a whole number of 1 KiB load instructions
 __host__ __device__ constexpr int rt_qslot(int G) { return G * kHeadDim * 2 > 1024 ? G * kHeadDim * 2 : 1024; }
 __host__ __device__ constexpr int rt_lds_fixed(int G) { return kRTKv * (kRTRing + kRTStages * rt_qslot(G)); }
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
     int32_t* __restrict__ header, float* __restrict__ part_ml, float* __restrict__ part_o, const NewRows nr) {
   constexpr int HQ = G * kRTKv;
   constexpr int QS = rt_qslot(G);
-  // eight wavefront V rings, eight wavefronts' query slots (one per stage), then the tile prefix
+  // eight wavefronts' K and V rows of the computing tile, their query slots (one per stage), then the tile prefix
   extern __shared__ __attribute__((aligned(16))) char rt_lds[];
   int* pre = reinterpret_cast<int*>(rt_lds + rt_lds_fixed(G));
 
@@ -864,7 +864,8 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
   const int grp = lane >> 4;   // lane group: keys 4 grp .. 4 grp + 3 of the S^T tile
   const bool row_real = col < G;
   const uint32_t nblk32 = num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)num_blocks;
-  char* ring = rt_lds + g * kRTRing;
+  char* kst = rt_lds + g * kRTRing;
+  char* vst = kst + kRTVSlice;
   char* qslots = rt_lds + kRTKv * kRTRing + g * (kRTStages * QS);
 
   // sequence holding global tile s0: pre[lo] <= s0 < pre[lo + 1]
@@ -897,56 +898,35 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
     return make_tile(nb < num_seqs ? nb : t.b, 0);  // past the last sequence only when the range ends there
   };
 
-  // Loads of a tile into ring stage ST (the cache rows are read once: nontemporal loads, which streamed 7-9 %
-  // faster than plain ones): head g's V rows into LDS (buffer loads with the lds bit, four 1 KiB
-  // instructions; instruction j writes tokens 4 j .. 4 j + 3, lane l token 4 j + grp, LDS chunk col, which
-  // holds logical chunk col ^ (4 token % 16)), issued first, then head g's K rows into registers in the MFMA A
-  // layout (lane l: key col, dims 32 kk + 8 grp .. + 7). Tokens past the context load its last row; with the
-  // fused store, the sequence's new token (its last position) comes from the step's input row. Buffer loads
-  // (not global_load_lds) keep the compiler's vmcnt accounting exact: it treats an LDS-writing global
-  // instruction like a flat access and then waits for every load in flight.
+  // Loads of a tile into the registers of stage ST: instruction j, lane l reads token 4 j + grp, the 16-byte
+  // chunk that belongs at LDS chunk col of that row (logical chunk col ^ (token % 16) for K, col ^ (4 token % 16)
+  // for V), so one 16-lane group reads a whole 256-byte row. The cache rows are read once: nontemporal loads
+  // (7-9 % faster than plain ones). Tokens past the context load its last row; with the fused store, the
+  // sequence's new token (its last position) comes from the step's input row. (Loads that write LDS directly
+  // would keep registers free, but the compiler treats an LDS-writing global instruction like a flat access and
+  // then waits for every load in flight; and K read straight into the MFMA layout, 64 bytes of 16 rows per
+  // instruction, streamed 3-4 % slower than whole rows.)
   u32x4 kreg[kRTStages][4];
+  u32x4 vreg[kRTStages][4];
   auto issue = [&](auto stage_c, const RowTile& t) {
     constexpr int ST = decltype(stage_c)::value;
     const int64_t row0 = (int64_t)t.blk * kBlockSize + (t.tok0 & (kBlockSize - 1));
     const bool from_input = FUSED && nr.k && t.last;
     const int t_new = t.nvalid - 1;
-    char* vst = ring + ST * kRTVSlice;
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + row0 * kRTRow + g * (kHeadDim * 2)), (short)0,
-                                          kRT * kRTRow, 0x00020000);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wold-style-cast"
-    if (!from_input) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tr = 4 * j + grp;
-        const int te = tr < t.nvalid ? tr : t_new;
-        const uint32_t off = (uint32_t)(te * kRTRow + 16 * (col ^ ((4 * tr) & 15)));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vst + 1024 * j), 16, off, 0, 0, kNtAux);
-      }
-    } else {
-      const __amdgpu_buffer_rsrc_t vi = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(nr.v + (int64_t)t.b * nr.v_stride_b + g * (kHeadDim * 2)), (short)0, kHeadDim * 2, 0x00020000);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tr = 4 * j + grp;
-        const int te = tr < t.nvalid ? tr : t_new;
-        const uint32_t ch16 = (uint32_t)(16 * (col ^ ((4 * tr) & 15)));
-        if (te != t_new)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(vst + 1024 * j), 16, (uint32_t)(te * kRTRow) + ch16,
-                                                   0, 0, kNtAux);
-        else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(vi, (lds_void_t*)(vst + 1024 * j), 16, ch16, 0, 0, 0);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int tr = 4 * j + grp;
+      const int te = tr < t.nvalid ? tr : t_new;
+      const bool inp = from_input && te == t_new;
+      const int kch = col ^ (tr & 15);
+      const int vch = col ^ ((4 * tr) & 15);
+      const char* ks = inp ? nr.k + (int64_t)t.b * nr.k_stride_b + g * (kHeadDim * 2) + 16 * kch
+                           : k_cache + (row0 + te) * kRTRow + g * (kHeadDim * 2) + 16 * kch;
+      const char* vs = inp ? nr.v + (int64_t)t.b * nr.v_stride_b + g * (kHeadDim * 2) + 16 * vch
+                           : v_cache + (row0 + te) * kRTRow + g * (kHeadDim * 2) + 16 * vch;
+      kreg[ST][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks));
+      vreg[ST][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs));
     }
-#pragma clang diagnostic pop
-    const int te = col < t.nvalid ? col : t_new;
-    const char* kp = (from_input && te == t_new)
-                         ? nr.k + (int64_t)t.b * nr.k_stride_b + g * (kHeadDim * 2) + 16 * grp
-                         : k_cache + (row0 + te) * kRTRow + g * (kHeadDim * 2) + 16 * grp;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) kreg[ST][kk] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 64 * kk));
     // the sequence's G query rows of this head group into the stage's query slot (lane l of instruction j:
     // row 4 j + grp, 16-byte chunk col, LDS offset 256 row + 16 col)
     if (t.qload) {
@@ -1017,13 +997,22 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
 
   auto compute = [&](auto stage_c, const RowTile& t, int gi) {
     constexpr int ST = decltype(stage_c)::value;
-    const char* vst = ring + ST * kRTVSlice;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *reinterpret_cast<u32x4*>(kst + 1024 * j + 16 * lane) = kreg[ST][j];
+      *reinterpret_cast<u32x4*>(vst + 1024 * j + 16 * lane) = vreg[ST][j];
+    }
+    __asm__ volatile("" ::: "memory");  // the operand reads below (one through a restrict pointer) follow these stores
+    u32x4 kop[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      kop[kk] = *reinterpret_cast<const u32x4*>(kst + col * (kHeadDim * 2) + 16 * ((4 * kk + grp) ^ col));
     if (t.qload) read_q(ST);
     // S^T = K_g Q^T (16 keys x 16 query rows)
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[ST][kk]),
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[kk]),
                                                   __builtin_bit_cast(bf16x8, qreg[kk]), s, 0, 0, 0);
     // lane l holds keys 4 grp + i (i = 0..3) of query row col; keys past the context are masked
     float x[4];
@@ -1057,7 +1046,7 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
       const uint2 va = rt_read_tr16(vrow + 16 * ((2 * db + (vc >> 1)) ^ ((4 * vk) & 15)));
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, va), pb4, acc[db], 0, 0, 0);
     }
-    // fused store: head g's K (from registers) and V (from the ring) of the sequence's new token go to its slot
+    // fused store: head g's K (from the operand registers) and V (from LDS) of the sequence's new token go to its slot
     if constexpr (FUSED) {
       if (nr.k && t.last) {
         const int32_t slot = nr.slots[t.b];
@@ -1067,7 +1056,7 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
           if (col == tn) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-              *reinterpret_cast<u32x4*>(nr.k_cache + dst + 64 * kk + 16 * grp) = kreg[ST][kk];
+              *reinterpret_cast<u32x4*>(nr.k_cache + dst + 64 * kk + 16 * grp) = kop[kk];
           }
           if (grp == 0)
             *reinterpret_cast<u32x4*>(nr.v_cache + dst + 16 * col) =
@@ -1083,7 +1072,7 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
     }
   };
 
-  // i-th tile of the range in ring stage ST: issue the tile two ahead into the stage freed by tile i - 1
+  // i-th tile of the range in stage ST: issue the tile two ahead into the stage freed by tile i - 1
   // (past the range end the last tile again, so every iteration issues the same eight loads), wait until
   // tile i's loads have landed (vmcnt counts this wavefront's memory operations in order: the sixteen loads of
   // the two tiles after it may still be in flight), then compute it
@@ -1212,7 +1201,8 @@ const void* rowtile_kernel() {
 
 size_t rowtile_lds(int G, int num_seqs) { return (size_t)rt_lds_fixed(G) + (size_t)(num_seqs + 1) * 4; }
 
-// Resident work-groups of the row-tile kernel (one per CU: its V rings and query slots take 144 KiB).
+// Resident work-groups of the row-tile kernel (one per CU: 212 registers per lane allow two wavefronts per
+// SIMD; its LDS rows and query slots take 112 KiB).
 int rowtile_grid(int G, int num_seqs) { return resident_wgs(rowtile_kernel<8, false>(), rowtile_lds(G, num_seqs), 512); }
 
 // Whether the row-tile kernel takes a call with these heads and sequences (eight query heads per KV head,
