@@ -738,14 +738,16 @@ def test_binding_launches_on_current_stream():
     assert torch.equal(kflat[rows].view(torch.int16), key.view(torch.int16))
 
 
-@pytest.mark.parametrize("hq,form", [(16, "auto"), (16, "rowwide"), (64, "auto")])
+@pytest.mark.parametrize("hq,form", [(16, "auto"), (16, "rowwide"), (64, "auto"), (64, "rowtile")])
 def test_decode_graphs_replay_matches_eager(hq, form, monkeypatch):
     """Decode-step graphs (the fused store + decode per bucket) give the bits
     of the eager kv_store and paged_attn_decode calls on the same static buffers, for batches that hit an exact
     bucket and batches that need padding rows; each graph is replayed three
     times with unrelated eager work and synchronisation in between, and the
     real rows are also checked against the oracle. These batches are small enough for the MFMA tile form of
-    decode (split over the keys with a merge); with 16 query heads they also run in the row-wide form."""
+    decode (split over the keys with a merge), except that with 64 query heads the 64-row bucket takes the
+    row-tile kernel; with 16 query heads they also run in the row-wide form, with 64 all on the row-tile
+    kernel."""
     if form != "auto":
         monkeypatch.setenv("PKV_DECODE_FORM", form)
     import paged_kv_attention_28_amd as P
