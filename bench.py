@@ -314,6 +314,13 @@ def cpu_baseline() -> dict:
 # GPU timing
 # ----------------------------------------------------------------------------
 
+def timing_event():
+    """A HIP timing event without the system-scope fence (harness.TimingEvent): the markers around the timed
+    calls then do not write back and invalidate the caches."""
+    from paged_kv_attention_28_amd import harness as H
+    return H.TimingEvent()
+
+
 def time_steps(runner, steps: int, warmup: int, torch):
     """Wall-clock K steps bracketed by synchronize; HIP events around the
     store and the attention call of every step (on the launch stream)."""
@@ -321,7 +328,7 @@ def time_steps(runner, steps: int, warmup: int, torch):
     for _ in range(warmup):
         runner.step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[timing_event() for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         k = runner.prepare_and_upload(record_guard=False)
@@ -348,7 +355,7 @@ def fused_steps(runner, steps: int, warmup: int, torch):
         runner.prepare_and_upload()
         runner.fused_only()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    evs = [[timing_event() for _ in range(2)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         k = runner.prepare_and_upload(record_guard=False)
@@ -370,7 +377,7 @@ def cold_warm(torch, runner, call_bytes: int, reps: int = 50) -> dict:
     flush = torch.empty(2**30 // 4, dtype=torch.int32, device=runner.q.device)
     out = {}
     for mode in ("cold", "warm"):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        ev = [[timing_event() for _ in range(2)] for _ in range(reps)]
         runner.fused_only()
         for i, e in enumerate(ev):
             if mode == "cold":
@@ -399,7 +406,7 @@ def rope_store_rate(torch, w, runner, reps: int):
     posd = torch.from_numpy(pos).to(runner.q.device)
     q = runner.q.clone()
     slots = runner.dev_meta[0]
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    ev = [[timing_event() for _ in range(2)] for _ in range(reps)]
     for _ in range(3):
         B.rope_kv_store(q, runner.k, runner.v, posd, tab, runner.dw.k_cache, runner.dw.v_cache, slots)
     for e in ev:
@@ -429,7 +436,7 @@ def copy_ceiling(torch, dev, reps: int = 10) -> dict:
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = timing_event(), timing_event()
         e0.record()
         for _ in range(reps):
             fn()
@@ -448,7 +455,7 @@ def back_to_back(torch, runner, seconds: float = 0.1) -> float:
     shader clock settles), on the metadata the runner last uploaded."""
     runner.attention_only()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = timing_event(), timing_event()
     e0.record()
     for _ in range(10):
         runner.attention_only()
@@ -561,7 +568,7 @@ def sampler_rate(torch, dev, reps: int = 20):
     ws = torch.empty(B.sample_temperature_workspace_size(rows, vocab), dtype=torch.uint8, device=dev)
     for _ in range(3):
         B.sample_temperature(out, logits, temps, noise, ws)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+    ev = [[timing_event() for _ in range(2)] for _ in range(reps)]
     for e in ev:
         e[0].record()
         B.sample_temperature(out, logits, temps, noise, ws)
@@ -633,7 +640,7 @@ def decode_gqa8(torch, dev, reps: int = 30) -> dict:
     for _ in range(5):
         call()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = timing_event(), timing_event()
     e0.record()
     for _ in range(reps):
         call()
@@ -759,7 +766,7 @@ def trace_small_batch_graphs(torch, max_rows: int = 64) -> dict:
             q, k, v = runner.values(i, layer, rows)
             b["q"][:rows], b["key"][:rows], b["value"][:rows] = q, k, v
         for mode in ("eager", "graph"):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = timing_event(), timing_event()
             e0.record()
             if mode == "eager":
                 for b, (kc, vc) in zip(bufs, runner.caches):
