@@ -181,7 +181,7 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * partials (at most about 6.5 MB) go to the workspace and are merged by a
  * second kernel in chunk order; the chunking depends only on num_seqs,
  * num_kv_heads and max_context_len. With eight KV heads, eight query heads
- * per KV head take a third kernel on calls of num_seqs >= 64 with
+ * per KV head take a third kernel on calls of num_seqs >= 48 with
  * max_context_len > 1024, or num_seqs >= 8 with max_context_len > 4096 (and
  * num_seqs <= 4000): stream-K over 16-token tiles, one work-group of eight
  * wavefronts per CU (one per KV head), its partials (64 query heads x 1040

@@ -78,7 +78,7 @@ constexpr int kTileMidCtx = 2048;
 // eight query heads per KV head: calls of at least kRowTileSeqs sequences with max_context_len above
 // kRowTileCtx, or of at least kRowTileLongSeqs with max_context_len above kRowTileLongCtx, take the row-tile
 // kernel; the rest the tile form
-constexpr int kRowTileSeqs = 64;
+constexpr int kRowTileSeqs = 48;
 constexpr int kRowTileCtx = 1024;
 constexpr int kRowTileLongSeqs = 8;
 constexpr int kRowTileLongCtx = 4096;
@@ -1300,9 +1300,10 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   // 5-13 % slower.
   // With eight query heads per KV head and eight KV heads, calls that stream longer contexts over enough
   // sequences take the row-tile kernel (decode_rowtile_kernel): a 28-layer decode step with the store fused,
-  // each layer its own caches, 64 Q / 8 KV, tile form -> row-tile kernel: contexts of 100-2048 tokens, 64-256
-  // sequences 6-12 % faster, 32 or fewer 6-28 % slower; 1024-8192 tokens, 8-64 sequences 8-20 % faster;
-  // contexts of 100-1024 tokens level or slower at every batch size.
+  // each layer its own caches, 64 Q / 8 KV, tile form -> row-tile kernel: contexts of 100-2048 tokens, 40-48
+  // sequences 1-2 % faster, 64-256 6-12 % faster, 32 or fewer 6-28 % slower; 100-4096 tokens, 48 sequences 15 %
+  // faster, 16-32 3-9 % slower; 1024-8192 tokens, 8-64 sequences 8-20 % faster; contexts of 100-1024 tokens level
+  // or slower at every batch size.
   // PKV_DECODE_FORM=tile, =rowwide or =rowtile in the environment overrides the choice (read on every call;
   // for tests and tuning; eight query heads per KV head never take the row-wide kernel, and the row-tile
   // kernel needs eight KV heads)

@@ -400,7 +400,7 @@ def _boundary(n, hi, hq, seed):
 # calls on both sides of the rules that pick the decode form: two or four query heads per KV head take the tile
 # form for at most 4 sequences, or at most 48 (two) or 80 (four) with max_context_len <= 1024, and four also for
 # at most 32 with max_context_len <= 2048 (else the row-wide kernel); eight on
-# eight KV heads take the row-tile kernel for at least 64 sequences with max_context_len > 1024, or at least 8
+# eight KV heads take the row-tile kernel for at least 48 sequences with max_context_len > 1024, or at least 8
 # with max_context_len > 4096 (else the tile form): name -> (case, form the default dispatch must take, the
 # other form of the shape)
 DISPATCH_CASES = {
@@ -416,9 +416,9 @@ DISPATCH_CASES = {
     "g4_32seqs_2048": (_boundary(32, 2048, 32, 58), "tile", "rowwide"),
     "g4_33seqs_2048": (_boundary(33, 2048, 32, 59), "rowwide", "tile"),
     "g4_32seqs_2049": (_boundary(32, 2049, 32, 60), "rowwide", "tile"),
-    "g8_64seqs_1025": (_boundary(64, 1025, 64, 51), "rowtile", "tile"),
-    "g8_63seqs_2048": (_boundary(63, 2048, 64, 52), "tile", "rowtile"),
-    "g8_64seqs_1024": (_boundary(64, 1024, 64, 53), "tile", "rowtile"),
+    "g8_48seqs_1025": (_boundary(48, 1025, 64, 51), "rowtile", "tile"),
+    "g8_47seqs_2048": (_boundary(47, 2048, 64, 52), "tile", "rowtile"),
+    "g8_48seqs_1024": (_boundary(48, 1024, 64, 53), "tile", "rowtile"),
     "g8_8seqs_4097": (_boundary(8, 4097, 64, 54), "rowtile", "tile"),
     "g8_7seqs_4097": (_boundary(7, 4097, 64, 55), "tile", "rowtile"),
     "g8_8seqs_4096": (_boundary(8, 4096, 64, 56), "tile", "rowtile"),
