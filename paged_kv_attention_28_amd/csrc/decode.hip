@@ -734,16 +734,15 @@ __global__ __launch_bounds__(256) void decode_stream_kernel(
 //
 // A tile is 16 consecutive tokens of one sequence (inside one cache block).
 // The global tile list (sequences in order) is divided evenly over the
-// work-groups; every wavefront of a work-group walks the work-group's tiles
-// for its own KV head, on its own (no barrier in the loop), with two tiles
-// in flight while it computes a third: head g's K and V rows of a tile come
-// into registers with nontemporal loads, each 16-lane group reading one
-// whole 256-byte row, and the computing tile's rows are written to LDS
-// private to the wavefront, from which K is read back in the layout of the
-// MFMA A operand and the transposing LDS read forms V^T. The first tile of
-// each sequence also brings the sequence's eight query rows of the head
-// group into that stage's LDS slot (direct-to-LDS buffer loads), read into
-// registers once per sequence. S^T = K_g Q^T with
+// work-groups. A work-group moves its tiles' whole K and V rows (2 KiB per
+// token, all eight heads) into a two-stage LDS buffer with direct-to-LDS
+// buffer loads (nontemporal; each wavefront moves two tokens, 1 KiB per
+// instruction), one tile in flight while the previous one is computed, with
+// a barrier before and after each tile's computation; wavefront g reads head
+// g's 256-byte column of the rows: K in the layout of the MFMA A operand, V^T
+// through the transposing LDS read. The first tile of each sequence also
+// brings the sequence's eight query rows of the head group into registers.
+// S^T = K_g Q^T with
 // v_mfma_f32_16x16x32_bf16 (16 keys x 16 query rows, the G query heads of
 // the KV head padded to 16), an online softmax per query row across the four
 // lane groups that hold its 16 scores, and O^T += V_g^T P^T with
@@ -762,7 +761,7 @@ constexpr int kRT = 16;                             // tokens per row tile
 constexpr int kRTKv = 8;                            // KV heads (one wavefront each)
 constexpr int kRTRow = kRTKv * kHeadDim * 2;        // 2 KiB: one token's K (or V) row
 constexpr int kRTMinTiles = 2;                      // tiles per work-group at least
-constexpr int kRTMaxSeqs = 4000;                    // LDS scan capacity beside the tile rows and query slots
+constexpr int kRTMaxSeqs = 4000;                    // LDS scan capacity beside the two tile stages
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 template <int N>
@@ -824,12 +823,11 @@ struct RowTile {
   int qload;  // the wavefront starts this sequence here: its query rows come with the tile
 };
 
-constexpr int kRTStages = 3;                        // per wavefront: two tiles in flight, one computed
-constexpr int kRTVSlice = kRT * kHeadDim * 2;       // 4 KiB: one KV head's K (or V) rows of a tile
-constexpr int kRTRing = 2 * kRTVSlice;              // 8 KiB of LDS per wavefront: the computed tile's K and V
-// per-stage LDS slot for a wavefront's G query rows (256 B each), a whole number of 1 KiB load instructions
-__host__ __device__ constexpr int rt_qslot(int G) { return G * kHeadDim * 2 > 1024 ? G * kHeadDim * 2 : 1024; }
-__host__ __device__ constexpr int rt_lds_fixed(int G) { return kRTKv * (kRTRing + kRTStages * rt_qslot(G)); }
+constexpr int kNtAux = 2;                            // buffer-load cache policy: nontemporal
+constexpr int kRTStages = 2;                         // LDS stages: one tile loading while one is computed
+constexpr int kRTTileRows = kRT * kRTRow;            // 32 KiB: a tile's K (or V) rows, all eight heads
+constexpr int kRTStage = 2 * kRTTileRows;            // 64 KiB: K rows, then V rows
+__host__ __device__ constexpr int rt_lds_fixed(int) { return kRTStages * kRTStage; }
 
 template <int G, bool FUSED>
 __global__ __launch_bounds__(512) void decode_rowtile_kernel(
@@ -838,8 +836,7 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
     const int32_t* __restrict__ context_lens, int num_seqs, int64_t num_blocks, float scale_log2, int max_ctx,
     int32_t* __restrict__ header, float* __restrict__ part_ml, float* __restrict__ part_o, const NewRows nr) {
   constexpr int HQ = G * kRTKv;
-  constexpr int QS = rt_qslot(G);
-  // eight wavefronts' K and V rows of the computing tile, their query slots (one per stage), then the tile prefix
+  // two stages of a tile's K and V rows (all eight heads), then the tile prefix
   extern __shared__ __attribute__((aligned(16))) char rt_lds[];
   int* pre = reinterpret_cast<int*>(rt_lds + rt_lds_fixed(G));
 
@@ -864,9 +861,6 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
   const int grp = lane >> 4;   // lane group: keys 4 grp .. 4 grp + 3 of the S^T tile
   const bool row_real = col < G;
   const uint32_t nblk32 = num_blocks > 0x7fffffff ? 0x7fffffffu : (uint32_t)num_blocks;
-  char* kst = rt_lds + g * kRTRing;
-  char* vst = kst + kRTVSlice;
-  char* qslots = rt_lds + kRTKv * kRTRing + g * (kRTStages * QS);
 
   // sequence holding global tile s0: pre[lo] <= s0 < pre[lo + 1]
   int lo_b = 0, hi_b = num_seqs;
@@ -875,7 +869,7 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
     if (pre[mid] <= s0) lo_b = mid; else hi_b = mid;
   }
   // tile metadata is wave-uniform: the sequence index goes through readfirstlane so that its context length
-  // and block id are scalar loads (a vector load there would make the loop wait for every load in flight)
+  // and block id are scalar loads
   auto rfl = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
   auto make_tile = [&](int b, int st) -> RowTile {
     RowTile t;
@@ -898,61 +892,65 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
     return make_tile(nb < num_seqs ? nb : t.b, 0);  // past the last sequence only when the range ends there
   };
 
-  // Loads of a tile into the registers of stage ST: instruction j, lane l reads token 4 j + grp, the 16-byte
-  // chunk that belongs at LDS chunk col of that row (logical chunk col ^ (token % 16) for K, col ^ (4 token % 16)
-  // for V), so one 16-lane group reads a whole 256-byte row. The cache rows are read once: nontemporal loads
-  // (7-9 % faster than plain ones). Tokens past the context load its last row; with the fused store, the
-  // sequence's new token (its last position) comes from the step's input row. (Loads that write LDS directly
-  // would keep registers free, but the compiler treats an LDS-writing global instruction like a flat access and
-  // then waits for every load in flight; and K read straight into the MFMA layout, 64 bytes of 16 rows per
-  // instruction, streamed 3-4 % slower than whole rows.)
-  u32x4 kreg[kRTStages][4];
-  u32x4 vreg[kRTStages][4];
+  // Loads of a tile into LDS stage ST, shared by the work-group: the first tile of a sequence brings this
+  // wavefront's query rows into the stage's registers first; then wavefront w moves tokens 2 w and 2 w + 1 of
+  // the tile, K and V, each 2 KiB row as two 1 KiB buffer loads with the lds bit (nontemporal: the rows are
+  // read once). Lane l of half hf writes the row's LDS chunk 64 hf + l, i.e. head 4 hf + l / 16, physical chunk
+  // l % 16, which holds that head's logical chunk (l % 16) ^ (t % 16) of K and (l % 16) ^ (4 t % 16) of V.
+  // Tokens past the context load its last row; with the fused store, the sequence's new token (its last
+  // position) comes from the step's input row. (Buffer loads, not global_load_lds: the compiler treats an
+  // LDS-writing global instruction like a flat access and then waits for every load in flight. Each wavefront
+  // streaming its own head's 256-byte slices, two tiles in flight in registers and no barrier, ran 0-6 %
+  // slower.)
+  u32x4 qst[kRTStages][4];
   auto issue = [&](auto stage_c, const RowTile& t) {
     constexpr int ST = decltype(stage_c)::value;
+    if (t.qload) {
+      const uint16_t* qp = q + ((int64_t)t.b * HQ + g * G + (row_real ? col : 0)) * kHeadDim + 8 * grp;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qst[ST][kk] = row_real ? *reinterpret_cast<const u32x4*>(qp + 32 * kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+    char* kb = rt_lds + ST * kRTStage;
+    char* vb = kb + kRTTileRows;
     const int64_t row0 = (int64_t)t.blk * kBlockSize + (t.tok0 & (kBlockSize - 1));
     const bool from_input = FUSED && nr.k && t.last;
     const int t_new = t.nvalid - 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tr = 4 * j + grp;
-      const int te = tr < t.nvalid ? tr : t_new;
-      const bool inp = from_input && te == t_new;
-      const int kch = col ^ (tr & 15);
-      const int vch = col ^ ((4 * tr) & 15);
-      const char* ks = inp ? nr.k + (int64_t)t.b * nr.k_stride_b + g * (kHeadDim * 2) + 16 * kch
-                           : k_cache + (row0 + te) * kRTRow + g * (kHeadDim * 2) + 16 * kch;
-      const char* vs = inp ? nr.v + (int64_t)t.b * nr.v_stride_b + g * (kHeadDim * 2) + 16 * vch
-                           : v_cache + (row0 + te) * kRTRow + g * (kHeadDim * 2) + 16 * vch;
-      kreg[ST][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ks));
-      vreg[ST][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vs));
-    }
-    // the sequence's G query rows of this head group into the stage's query slot (lane l of instruction j:
-    // row 4 j + grp, 16-byte chunk col, LDS offset 256 row + 16 col)
-    if (t.qload) {
-      const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(q + ((int64_t)t.b * HQ + g * G) * kHeadDim), (short)0, G * kHeadDim * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(k_cache + row0 * kRTRow), (short)0, kRTTileRows, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(v_cache + row0 * kRTRow), (short)0, kRTTileRows, 0x00020000);
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Wold-style-cast"
 #pragma unroll
-      for (int j = 0; j < QS / 1024; ++j)
-        if (4 * j + grp < G)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void_t*)(qslots + ST * QS + 1024 * j), 16,
-                                                   (uint32_t)((4 * j + grp) * (kHeadDim * 2) + 16 * col), 0, 0, 0);
-#pragma clang diagnostic pop
-    }
-  };
-
-  // queries of the tile's sequence for the MFMA B operand, from the query slot of stage ST: lane l holds
-  // row l % 16 (query head g G + l % 16 when l % 16 < G, else zeros), dims 32 kk + 8 grp .. + 7
-  u32x4 qreg[4];
-  auto read_q = [&](int st_slot) {
-    const char* qp = qslots + st_slot * QS + (row_real ? col : 0) * (kHeadDim * 2) + 16 * grp;
+    for (int r = 0; r < 2; ++r) {
+      const int tr = 2 * g + r;
+      const int te = tr < t.nvalid ? tr : t_new;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      qreg[kk] = row_real ? *reinterpret_cast<const u32x4*>(qp + 64 * kk) : u32x4{0u, 0u, 0u, 0u};
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t hoff = (uint32_t)((4 * hf + grp) * (kHeadDim * 2));
+        const uint32_t kc = (uint32_t)(16 * (col ^ (tr & 15)));
+        const uint32_t vc = (uint32_t)(16 * (col ^ ((4 * tr) & 15)));
+        lds_void_t* kd = (lds_void_t*)(kb + tr * kRTRow + 1024 * hf);
+        lds_void_t* vd = (lds_void_t*)(vb + tr * kRTRow + 1024 * hf);
+        if (from_input && te == t_new) {
+          const __amdgpu_buffer_rsrc_t ki = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(nr.k + (int64_t)t.b * nr.k_stride_b), (short)0, kRTRow, 0x00020000);
+          const __amdgpu_buffer_rsrc_t vi = __builtin_amdgcn_make_buffer_rsrc(
+              (void*)(nr.v + (int64_t)t.b * nr.v_stride_b), (short)0, kRTRow, 0x00020000);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ki, kd, 16, hoff + kc, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vi, vd, 16, hoff + vc, 0, 0, 0);
+        } else {
+          const uint32_t roff = (uint32_t)(te * kRTRow) + hoff;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, kd, 16, roff + kc, 0, 0, kNtAux);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, vd, 16, roff + vc, 0, 0, kNtAux);
+        }
+      }
+    }
+#pragma clang diagnostic pop
   };
 
+  u32x4 qreg[4];
   f32x4 acc[8];
   float m_run, l_part;
   auto reset = [&]() {
@@ -997,17 +995,16 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
 
   auto compute = [&](auto stage_c, const RowTile& t, int gi) {
     constexpr int ST = decltype(stage_c)::value;
+    const char* kb = rt_lds + ST * kRTStage + g * (kHeadDim * 2);  // head g's 256-byte column of the rows
+    const char* vb = kb + kRTTileRows;
+    if (t.qload) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(kst + 1024 * j + 16 * lane) = kreg[ST][j];
-      *reinterpret_cast<u32x4*>(vst + 1024 * j + 16 * lane) = vreg[ST][j];
+      for (int kk = 0; kk < 4; ++kk) qreg[kk] = qst[ST][kk];
     }
-    __asm__ volatile("" ::: "memory");  // the operand reads below (one through a restrict pointer) follow these stores
     u32x4 kop[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      kop[kk] = *reinterpret_cast<const u32x4*>(kst + col * (kHeadDim * 2) + 16 * ((4 * kk + grp) ^ col));
-    if (t.qload) read_q(ST);
+      kop[kk] = *reinterpret_cast<const u32x4*>(kb + col * kRTRow + 16 * ((4 * kk + grp) ^ col));
     // S^T = K_g Q^T (16 keys x 16 query rows)
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1039,65 +1036,66 @@ __global__ __launch_bounds__(512) void decode_rowtile_kernel(
     // read; lane 4 k + c of a group names key 4 grp + k, dims 16 db + 4 c .. + 3
     const int vk = 4 * grp + ((lane & 15) >> 2);
     const int vc = lane & 3;
-    const char* vrow = vst + vk * (kHeadDim * 2) + 8 * (vc & 1);
+    const char* vrow = vb + vk * kRTRow + 8 * (vc & 1);
     const bf16x4 pb4 = __builtin_bit_cast(bf16x4, u32x2{w0, w1});
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const uint2 va = rt_read_tr16(vrow + 16 * ((2 * db + (vc >> 1)) ^ ((4 * vk) & 15)));
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, va), pb4, acc[db], 0, 0, 0);
     }
-    // fused store: head g's K (from the operand registers) and V (from LDS) of the sequence's new token go to its slot
+    // fused store: head g's K and V rows of the sequence's new token go from LDS to its slot
     if constexpr (FUSED) {
       if (nr.k && t.last) {
         const int32_t slot = nr.slots[t.b];
         const int tn = t.nvalid - 1;
-        if (slot >= 0 && (int64_t)slot < nr.num_slots) {
+        if (slot >= 0 && (int64_t)slot < nr.num_slots && grp == 0) {
           const int64_t dst = (int64_t)slot * kRTRow + g * (kHeadDim * 2);
-          if (col == tn) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-              *reinterpret_cast<u32x4*>(nr.k_cache + dst + 64 * kk + 16 * grp) = kop[kk];
-          }
-          if (grp == 0)
-            *reinterpret_cast<u32x4*>(nr.v_cache + dst + 16 * col) =
-                *reinterpret_cast<const u32x4*>(vst + tn * (kHeadDim * 2) + 16 * (col ^ ((4 * tn) & 15)));
+          *reinterpret_cast<u32x4*>(nr.k_cache + dst + 16 * (col ^ (tn & 15))) =
+              *reinterpret_cast<const u32x4*>(kb + tn * kRTRow + 16 * col);
+          *reinterpret_cast<u32x4*>(nr.v_cache + dst + 16 * (col ^ ((4 * tn) & 15))) =
+              *reinterpret_cast<const u32x4*>(vb + tn * kRTRow + 16 * col);
         }
       }
     }
     if (t.last || gi + 1 == s1) {
       finish_piece(t, gi);
       // vmcnt also counts stores, and loads and stores may complete out of order: wait here for the piece's
-      // stores (and the tiles in flight), so that the loop's waits can count the loads alone
+      // stores (and the tile in flight), so that the loop's waits can count the loads alone
       __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     }
   };
 
-  // i-th tile of the range in stage ST: issue the tile two ahead into the stage freed by tile i - 1
-  // (past the range end the last tile again, so every iteration issues the same eight loads), wait until
-  // tile i's loads have landed (vmcnt counts this wavefront's memory operations in order: the sixteen loads of
-  // the two tiles after it may still be in flight), then compute it
+  // i-th tile of the range in stage ST: issue tile i + 1 into the other stage (which the work-group finished
+  // reading at the end of the previous iteration; past the range end the last tile again, so every iteration
+  // issues the same eight K/V loads, after any query loads), wait for this wavefront's loads of tile i (vmcnt
+  // counts in order: only tile i + 1's eight K/V loads may still be in flight), then a barrier makes the whole
+  // tile visible; compute it, and a second barrier frees its stage for tile i + 2
+  // (a plain s_barrier: __syncthreads() would also wait for the next tile's loads; the empty asm statements
+  // keep the compiler from moving LDS accesses across it)
+  auto wg_barrier = []() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  };
   RowTile tl[kRTStages];
   auto iteration = [&](auto stage_c, int i) {
     constexpr int ST = decltype(stage_c)::value;
-    constexpr int NX = (ST + 2) % kRTStages;
-    const RowTile& prev = tl[(ST + 1) % kRTStages];
-    tl[NX] = i + 2 < n ? next_tile(prev) : prev;
+    constexpr int NX = ST ^ 1;
+    tl[NX] = i + 1 < n ? next_tile(tl[ST]) : tl[ST];
     issue(RTStage<NX>{}, tl[NX]);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(16));
-    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+    wg_barrier();
     if (i < n) compute(stage_c, tl[ST], s0 + i);
+    wg_barrier();
   };
 
   tl[0] = make_tile(lo_b, s0 - pre[lo_b]);
   tl[0].qload = 1;
   issue(RTStage<0>{}, tl[0]);
-  tl[1] = n > 1 ? next_tile(tl[0]) : tl[0];
-  issue(RTStage<1>{}, tl[1]);
   for (int i = 0; i < n; i += kRTStages) {
     iteration(RTStage<0>{}, i);
     iteration(RTStage<1>{}, i + 1);
-    iteration(RTStage<2>{}, i + 2);
   }
 }
 
@@ -1201,8 +1199,7 @@ const void* rowtile_kernel() {
 
 size_t rowtile_lds(int G, int num_seqs) { return (size_t)rt_lds_fixed(G) + (size_t)(num_seqs + 1) * 4; }
 
-// Resident work-groups of the row-tile kernel (one per CU: 212 registers per lane allow two wavefronts per
-// SIMD; its LDS rows and query slots take 112 KiB).
+// Resident work-groups of the row-tile kernel (one per CU: its two LDS stages take 128 KiB).
 int rowtile_grid(int G, int num_seqs) { return resident_wgs(rowtile_kernel<8, false>(), rowtile_lds(G, num_seqs), 512); }
 
 // Whether the row-tile kernel takes a call with these heads and sequences (eight query heads per KV head,
