@@ -177,6 +177,49 @@ def test_long_decode_sampled():
     torch.cuda.empty_cache()
 
 
+def test_gqa8_full_size_sampled(monkeypatch):
+    """The decode workload's shape with eight query heads per KV head (256 sequences of U[100, 2048] tokens + 16
+    padding rows, 64 Q / 8 KV: the bench's decode_gqa8 shape, which takes the row-tile kernel): 32 sequences
+    checked one by one against the oracle (the 8 longest, the 8 shortest and 16 drawn), padding rows zero, the
+    fused store call bit-identical to the separate store and call, and the tile form within tolerance too."""
+    from paged_kv_attention_28_amd import binding as B
+    w = W._decode_workload("decode_gqa8", W.SEEDS[2], 256, 100, 2048, 64, 16)
+    dw = H.DeviceWorkload(w).build()
+    p = w.passes[0]
+    q, m = dw.pass_inputs(p)
+    out = dw.run_pass(p, q, m)
+    torch.cuda.synchronize()
+    lens = np.asarray([s.seq_len for s in p.batch.seqs])
+    order = np.argsort(lens, kind="stable")
+    ends = [int(x) for x in order[-8:]] + [int(x) for x in order[:8]]
+    rest = np.setdiff1d(np.arange(len(lens)), ends)
+    idx = sorted(set(ends + [int(x) for x in np.random.default_rng(45).choice(rest, 16, replace=False)]))
+    print(f"[gqa8 full size] checking {len(idx)} sequences, contexts {lens[idx].min()}..{lens[idx].max()}", flush=True)
+    ref = O.decode_sampled(w, idx, device="cuda")
+    assert_close(out[idx], ref, None, "64 Q / 8 KV sampled decode")
+    assert (_f64(out[len(lens):]) == 0).all()
+    # the fused store + decode on a second copy of the pool gives the same output and caches
+    dw2 = H.DeviceWorkload(w)
+    dw2.run_setup()
+    k_new, v_new = W.store_kv(w, "cuda")
+    fused = torch.empty_like(q)
+    ws = H.decode_workspace(w, q.shape[0], m.max_context_len)
+    B.paged_attn_decode_store(fused, q, k_new, v_new, dw2.store_slots(), dw2.k_cache, dw2.v_cache, m.block_tables,
+                              m.context_lens, w.scale, m.max_context_len, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(dw2.k_cache.view(torch.int16), dw.k_cache.view(torch.int16))
+    assert torch.equal(dw2.v_cache.view(torch.int16), dw.v_cache.view(torch.int16))
+    del dw2
+    # the tile form on the same call
+    monkeypatch.setenv("PKV_DECODE_FORM", "tile")
+    tile = dw.run_pass(p, q, m)
+    torch.cuda.synchronize()
+    assert not torch.equal(tile.view(torch.int16), out.view(torch.int16)), "forms agree bit for bit"
+    assert_close(tile[idx], ref, None, "64 Q / 8 KV sampled decode, tile form")
+    torch.cuda.empty_cache()
+
+
 # ----------------------------------------------------------------------------
 # edge cases on small hand-built workloads
 # ----------------------------------------------------------------------------
