@@ -47,8 +47,9 @@
 //    written) and get a score of -inf: stale or poisoned cache rows never
 //    enter the result.
 //  * Eight query heads per KV head do eight times the arithmetic of one per
-//    byte, which bounds this kernel's vector FMAs; those calls run on the
-//    MFMA tile form of the prefill kernel instead (decode_tile_call).
+//    byte, which bounds this kernel's vector FMAs; those calls run on MFMA
+//    instead: the row-tile kernel below (eight KV heads, calls that stream
+//    enough) or the tile form of the prefill kernel (decode_tile_call).
 
 #include <cstdlib>
 #include <cstring>
@@ -1153,7 +1154,7 @@ const void* pick_kernel(int G, int hkv) {
     case 4: return stream_kernel<GG, 4>(); \
     default: return stream_kernel<GG, 8>(); \
   }
-  switch (G) {  // eight query heads per KV head run on the tile form (decode_tile_call)
+  switch (G) {  // eight query heads per KV head run on the row-tile kernel or the tile form
     case 1: PKV_PICK(1)
     case 2: PKV_PICK(2)
     default: PKV_PICK(4)
@@ -1284,9 +1285,10 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
       return fail(PKV_ERR_UNSUPPORTED, "paged_attn_decode: workspace must be 256-byte aligned");
   }
 
-  // The MFMA tile form (decode_tile_call) takes eight query heads per KV head, where the row-wide kernel
-  // below is bound by its vector arithmetic (4.0-4.3 TB/s), and small calls with two or four, where the
-  // row-wide kernel's fixed cost (two launches, a merge over pieces spread across all wavefronts) dominates.
+  // The MFMA forms take eight query heads per KV head (the tile form, decode_tile_call, or the row-tile
+  // kernel), where the row-wide kernel below is bound by its vector arithmetic (4.0-4.3 TB/s), and the tile
+  // form takes small calls with two or four, where the row-wide kernel's fixed cost (two launches, a merge over
+  // pieces spread across all wavefronts) dominates.
   // Measured on MI355X, 64 Q / 8 KV, row-wide -> tile form: 1 sequence of 100-2048 tokens 22.0 -> 13.1 us,
   // 16: 45.8 -> 20.7, 256: 282.5 -> 223.5 us; 4096-32768 tokens, 1 sequence 56.1 -> 45.8 us, 128: 2197 -> 1754
   // us. 16 Q / 8 KV, a 28-layer decode step with the store fused, each layer its own caches: contexts of
