@@ -614,7 +614,8 @@ def long_decode(torch, dev, steps: int, warmup: int) -> dict:
 def decode_gqa8(torch, dev, reps: int = 30) -> dict:
     """Decode with eight query heads per KV head (64 Q / 8 KV), 256 sequences of U[100, 2048] tokens on a
     shuffled pool: paged_attn_decode back to back (HIP events around `reps` calls on the stream). This shape
-    runs on the row-tile kernel (eight wavefronts per CU, one per KV head, streaming 16-token tiles)."""
+    runs on the row-tile kernel (a work-group of eight wavefronts per CU moves 16-token tiles of whole K/V rows
+    into LDS; wavefront g computes KV head g)."""
     from paged_kv_attention_28_amd import binding as B
     rng = np.random.default_rng(8)
     S, hq, hkv, d = 256, 64, 8, 128
@@ -655,7 +656,7 @@ def decode_gqa8(torch, dev, reps: int = 30) -> dict:
     return {"workload": "decode, 256 seqs, context U[100, 2048], GQA 64Q/8KV (eight query heads per KV head), "
                         "head_dim 128, bf16, block 256, shuffled pool; paged_attn_decode back to back",
             "us": round(us, 2), "gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes": byts, "form": "row-tile kernel (stream-K over 16-token tiles, one wavefront per KV head)"}
+            "algorithmic_bytes": byts, "form": "row-tile kernel (stream-K over 16-token tiles of whole K/V rows in LDS, one wavefront per KV head)"}
 
 
 def graph_vs_eager(torch, dev, iters: int = 50, num_layers: int = 28):
