@@ -762,7 +762,7 @@ constexpr int kRT = 16;                             // tokens per row tile
 constexpr int kRTKv = 8;                            // KV heads (one wavefront each)
 constexpr int kRTRow = kRTKv * kHeadDim * 2;        // 2 KiB: one token's K (or V) row
 constexpr int kRTMinTiles = 2;                      // tiles per work-group at least
-constexpr int kRTMaxSeqs = 4000;                    // LDS scan capacity beside the two tile stages
+constexpr int kRTMaxSeqs = 8000;                    // LDS scan capacity beside the two tile stages
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 template <int N>

@@ -312,10 +312,10 @@ EDGE = {
     "decode_tile_split_hkv1": _dec([5, 2500, 777], hq=8, hkv=1),
     # eight query heads on eight KV heads, the row-tile kernel's edges: contexts on both sides of its 16-token
     # tiles and of a cache block, sequence ends inside every work-group's range, padding rows, more than 32
-    # sequences (serial merge); the most sequences its LDS scan holds (4000)
+    # sequences (serial merge); the most sequences its LDS scan holds (8000)
     "decode_rowtile_ragged": _dec([1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 3000, 1025]
                                   + [(89 * i) % 2200 + 1 for i in range(88)], hq=64, pad=2),
-    "decode_rowtile_4000seqs": _dec([(13 * i) % 40 + 1 for i in range(4000)], hq=64),
+    "decode_rowtile_8000seqs": _dec([(13 * i) % 40 + 1 for i in range(8000)], hq=64),
     # more than 32 sequences with 8 and 4 query heads: the per-sequence (serial) merge
     "decode_hq8_hkv4_40seqs": _dec([(41 * i) % 900 + 1 for i in range(40)], hq=8, hkv=4),
     "decode_hq4_hkv1_40seqs": _dec([(29 * i) % 1300 + 1 for i in range(40)], hq=4, hkv=1),
