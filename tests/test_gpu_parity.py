@@ -493,6 +493,32 @@ def test_decode_dispatch_boundaries(name, monkeypatch):
         assert_close(out, ref, m.host.cu_seqlens_q, f"{name} ({form})")
 
 
+def test_decode_rowtile_sequence_limit(monkeypatch):
+    """Eight query heads on eight KV heads in calls that the form rule gives the row-tile kernel (at least 128
+    sequences, max_context_len above 512): 8000 sequences run there, 8001 -- past what its LDS holds of the
+    sequences' tile prefix -- on the tile form, also with the row-tile kernel forced; both match the oracle."""
+    for n, expect in ((8000, "rowtile"), (8001, "tile")):
+        lens = [(13 * i) % 40 + 1 for i in range(n - 1)] + [600]
+        w = custom(**_dec(lens, hq=64, seed=70 + n % 2))
+        dw = H.DeviceWorkload(w).build()
+        p = w.passes[0]
+        q, m = dw.pass_inputs(p)
+        print(f"[rowtile limit] {n} sequences", flush=True)
+        outs = {}
+        for form in ("auto", "tile", "rowtile"):
+            monkeypatch.setenv("PKV_DECODE_FORM", form)
+            outs[form] = dw.run_pass(p, q, m).clone()
+        monkeypatch.delenv("PKV_DECODE_FORM")
+        assert torch.equal(outs["auto"].view(torch.int16), outs[expect].view(torch.int16)), f"{n}: not {expect}"
+        if n > 8000:
+            assert torch.equal(outs["rowtile"].view(torch.int16), outs["tile"].view(torch.int16)), \
+                f"{n}: the forced row-tile call did not fall back to the tile form"
+        kc, vc = O.build_caches(w, device="cuda")
+        ref = O.run_pass(w, p, kc, vc, q=q)
+        assert_close(outs["auto"], ref, m.host.cu_seqlens_q, f"{n} sequences")
+        del dw, kc, vc
+
+
 FUSED_CASES = ["config2", "decode_len1", "decode_pad_rows", "decode_gqa1", "decode_gqa4", "decode_gqa8", "decode_hkv1",
                "decode_hq64", "decode_hq64_40seqs", "decode_long_ctx", "decode_peaky_gqa4_long", "decode_ramp_gqa8",
                "decode_hkv4_gqa2", "decode_hkv4_gqa4_long", "decode_hq8_hkv4_40seqs", "decode_tile_gqa8_pad",
