@@ -182,8 +182,9 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads,
  * second kernel in chunk order; the chunking depends only on num_seqs,
  * num_kv_heads and max_context_len. With eight KV heads, eight query heads
  * per KV head take a third kernel on calls of num_seqs >= 48 with
- * max_context_len > 1024, num_seqs >= 8 with max_context_len > 4096, or
- * num_seqs >= 128 with max_context_len > 512 (and num_seqs <= 8000): stream-K over 16-token tiles, one work-group of eight
+ * max_context_len > 1024, num_seqs >= 8 with max_context_len > 4096,
+ * num_seqs >= 80 with max_context_len > 768, or num_seqs >= 128 with
+ * max_context_len > 512 (and num_seqs <= 8000): stream-K over 16-token tiles, one work-group of eight
  * wavefronts per CU (one per KV head), its partials (64 query heads x 1040
  * bytes per work-group) merged by the stream-K kernel's merge; the split
  * depends only on the context lengths, max_context_len and the CU count.

@@ -77,12 +77,15 @@ constexpr int kTileShortCtx = 1024;
 constexpr int kTileMidSeqsG4 = 32;
 constexpr int kTileMidCtx = 2048;
 // eight query heads per KV head: calls of at least kRowTileSeqs sequences with max_context_len above
-// kRowTileCtx, of at least kRowTileLongSeqs with max_context_len above kRowTileLongCtx, or of at least
-// kRowTileManySeqs with max_context_len above kRowTileManyCtx take the row-tile kernel; the rest the tile form
+// kRowTileCtx, of at least kRowTileLongSeqs with max_context_len above kRowTileLongCtx, of at least
+// kRowTileMidSeqs with max_context_len above kRowTileMidCtx, or of at least kRowTileManySeqs with
+// max_context_len above kRowTileManyCtx take the row-tile kernel; the rest the tile form
 constexpr int kRowTileSeqs = 48;
 constexpr int kRowTileCtx = 1024;
 constexpr int kRowTileLongSeqs = 8;
 constexpr int kRowTileLongCtx = 4096;
+constexpr int kRowTileMidSeqs = 80;
+constexpr int kRowTileMidCtx = 768;
 constexpr int kRowTileManySeqs = 128;
 constexpr int kRowTileManyCtx = 512;
 // LDS reserved per stream work-group: more than half a CU's 160 KiB, so each
@@ -1300,13 +1303,15 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
   // 100-2048 tokens, 8-32 sequences 1-12 % faster, 48 and 64 4-13 % slower; 100-4096 tokens, 8-32 sequences
   // 5-13 % slower.
   // With eight query heads per KV head and eight KV heads, calls that stream longer contexts over enough
-  // sequences, or contexts beyond 512 tokens over many sequences, take the row-tile kernel (decode_rowtile_kernel): a 28-layer decode step with the store fused,
+  // sequences, or shorter contexts (beyond 768 or 512 tokens) over more sequences, take the row-tile kernel (decode_rowtile_kernel): a 28-layer decode step with the store fused,
   // each layer its own caches, 64 Q / 8 KV, tile form -> row-tile kernel: contexts of 100-2048 tokens, 40-48
   // sequences 1-2 % faster, 64-256 6-12 % faster, 32 or fewer 6-28 % slower; 100-4096 tokens, 48 sequences 15 %
   // faster, 16-32 3-9 % slower; 1024-8192 tokens, 8-64 sequences 8-20 % faster; 100-1024 tokens, 48 sequences
-  // 5 % slower, 64-96 4-7 % faster; 512-1024 tokens, 48-64 sequences 3 % slower, 96 level; at 128 sequences and
-  // more, contexts of 100-640, 100-768, 100-1024, 256-768, 400-640 and 512-1024 tokens 2-10 % faster (up to 1024
-  // sequences; 256 of 100-640 tokens 2 % slower), 100-512 tokens 128-256 sequences 4 % faster to 6 % slower.
+  // 5 % slower, 64-112 3-7 % faster; 512-1024 tokens, 48-64 sequences 3 % slower, 80-112 2-9 % faster; 256-1024
+  // and 700-1024 tokens, 80 sequences 7-9 % faster; 100-900 tokens, 80 sequences 3 % slower, 96 3 % faster; at 128
+  // sequences and more, contexts of 100-640, 100-768, 100-1024, 256-768, 400-640 and 512-1024 tokens 2-10 % faster
+  // (up to 1024 sequences; 256 of 100-640 tokens 2 % slower), 100-512 tokens 128-256 sequences 4 % faster to 6 %
+  // slower.
   // PKV_DECODE_FORM=tile, =rowwide or =rowtile in the environment overrides the choice (read on every call;
   // for tests and tuning; eight query heads per KV head never take the row-wide kernel, and the row-tile
   // kernel needs eight KV heads)
@@ -1323,6 +1328,7 @@ pkv_status decode_call(void* out, const void* q, const void* k_cache, const void
                           (int64_t)num_seqs * ((max_context_len + kRT - 1) / kRT) <= INT32_MAX;
   const bool rowtile_pick = G == 8 && ((num_seqs >= kRowTileSeqs && max_context_len > kRowTileCtx) ||
                                        (num_seqs >= kRowTileLongSeqs && max_context_len > kRowTileLongCtx) ||
+                                       (num_seqs >= kRowTileMidSeqs && max_context_len > kRowTileMidCtx) ||
                                        (num_seqs >= kRowTileManySeqs && max_context_len > kRowTileManyCtx));
   if (rowtile_ok && (force_rowtile || (rowtile_pick && !force_tile))) {
     const int grid = rowtile_grid(G, num_seqs);

@@ -444,8 +444,8 @@ def _boundary(n, hi, hq, seed):
 # form for at most 4 sequences, or at most 48 (two) or 80 (four) with max_context_len <= 1024, and four also for
 # at most 32 with max_context_len <= 2048 (else the row-wide kernel); eight on
 # eight KV heads take the row-tile kernel for at least 48 sequences with max_context_len > 1024, at least 8
-# with max_context_len > 4096, or at least 128 with max_context_len > 512 (else the tile form): name -> (case,
-# form the default dispatch must take, the other form of the shape)
+# with max_context_len > 4096, at least 80 with max_context_len > 768, or at least 128 with max_context_len > 512
+# (else the tile form): name -> (case, form the default dispatch must take, the other form of the shape)
 DISPATCH_CASES = {
     "g2_4seqs_2048": (_boundary(4, 2048, 16, 41), "tile", "rowwide"),
     "g2_5seqs_2048": (_boundary(5, 2048, 16, 42), "rowwide", "tile"),
@@ -466,8 +466,11 @@ DISPATCH_CASES = {
     "g8_7seqs_4097": (_boundary(7, 4097, 64, 55), "tile", "rowtile"),
     "g8_8seqs_4096": (_boundary(8, 4096, 64, 56), "tile", "rowtile"),
     "g8_128seqs_513": (_boundary(128, 513, 64, 61), "rowtile", "tile"),
-    "g8_127seqs_1024": (_boundary(127, 1024, 64, 62), "tile", "rowtile"),
+    "g8_127seqs_768": (_boundary(127, 768, 64, 62), "tile", "rowtile"),
     "g8_128seqs_512": (_boundary(128, 512, 64, 63), "tile", "rowtile"),
+    "g8_80seqs_769": (_boundary(80, 769, 64, 64), "rowtile", "tile"),
+    "g8_79seqs_1024": (_boundary(79, 1024, 64, 65), "tile", "rowtile"),
+    "g8_80seqs_768": (_boundary(80, 768, 64, 66), "tile", "rowtile"),
 }
 
 
